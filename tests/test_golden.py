@@ -1,0 +1,33 @@
+"""Stored oracle values for the tiny workload still match (guards the generator and oracle)."""
+import os
+
+import numpy as np
+
+from oracle import ref
+from ragged_attention_serving_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def load_golden():
+    rows = np.loadtxt(os.path.join(HERE, "golden", "tiny_cross_f32.txt"))
+    return rows
+
+
+def test_tiny_cross_golden():
+    g = load_golden()
+    w = synth.tiny_cross(0)
+    out, lse = ref.run_workload(w)
+    for row in g:
+        i, h = int(row[0]), int(row[1])
+        assert abs(lse[i, h] - row[2]) < 1e-13
+        assert np.allclose(out[i, h], row[3:], atol=1e-13, rtol=0)
+
+
+def test_generator_self_check():
+    """Lengths of the seeded workloads (the survey's self-check values)."""
+    w3 = synth.ragged_prefill(0)
+    assert int(w3.qo_indptr[-1]) == 7569 and list(w3.qo_lens()[:4]) == [382, 286, 229, 121]
+    assert w3.k_pages.shape == (3008, 16, 20, 64)
+    w1 = synth.tiny_cross(0)
+    assert list(w1.kv_lens()) == [16, 40] and w1.k_pages.shape == (14, 4, 2, 16)

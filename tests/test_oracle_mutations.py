@@ -1,0 +1,140 @@
+"""Plant plausible mistakes in copies of the oracle; each must trip at least one pin.
+
+The mistakes are planted in the oracle only, on the CPU, by swapping one of its
+functions for a broken variant for the duration of one check.
+"""
+import numpy as np
+import pytest
+
+import oracle.ref as ref
+from tests import oracle_pins
+
+_orig = {n: getattr(ref, n) for n in ("to_f64", "request_lengths", "gather_pages", "visible",
+                                      "attend", "merge_states")}
+
+
+def _gather_reversed_pages(pool, kv_indptr, kv_page_indices, r, kv_len, page_size, kv_head):
+    lo, hi = int(kv_indptr[r]), int(kv_indptr[r + 1])
+    pages = np.arange(lo, hi) if kv_page_indices is None else np.asarray(kv_page_indices[lo:hi])
+    rows = pool[pages[::-1], :, kv_head, :]
+    return rows.reshape(-1, rows.shape[-1])[:kv_len]
+
+
+def _gather_ignores_table(pool, kv_indptr, kv_page_indices, r, kv_len, page_size, kv_head):
+    return _orig["gather_pages"](pool, kv_indptr, None, r, kv_len, page_size, kv_head)
+
+
+def _gather_wrong_head(pool, kv_indptr, kv_page_indices, r, kv_len, page_size, kv_head):
+    return _orig["gather_pages"](pool, kv_indptr, kv_page_indices, r, kv_len, page_size,
+                                 (kv_head + 1) % pool.shape[2])
+
+
+def _visible_top_left(mask_mode, qo_len, kv_len, block_size):
+    if mask_mode == ref.MASK_NONE:
+        return np.ones((qo_len, kv_len), bool)
+    j = np.arange(kv_len)[None, :]
+    i = np.arange(qo_len)[:, None]
+    return j <= i if mask_mode == ref.MASK_CAUSAL else (j // block_size) <= (i // block_size)
+
+
+def _visible_block_strict(mask_mode, qo_len, kv_len, block_size):
+    if mask_mode != ref.MASK_BLOCK_CAUSAL:
+        return _orig["visible"](mask_mode, qo_len, kv_len, block_size)
+    j = np.arange(kv_len)[None, :]
+    p = (kv_len - qo_len + np.arange(qo_len))[:, None]
+    return (j // block_size) < (p // block_size) + (j <= p)  # own block only up to the diagonal
+
+
+def _visible_causal_off_by_one(mask_mode, qo_len, kv_len, block_size):
+    if mask_mode != ref.MASK_CAUSAL:
+        return _orig["visible"](mask_mode, qo_len, kv_len, block_size)
+    j = np.arange(kv_len)[None, :]
+    p = (kv_len - qo_len + np.arange(qo_len))[:, None]
+    return j < p
+
+
+def _attend_no_scale(Q, K, V, vis, scale):
+    return _orig["attend"](Q, K, V, vis, 1.0)
+
+
+def _attend_lse_without_max(Q, K, V, vis, scale):
+    O, lse = _orig["attend"](Q, K, V, vis, scale)
+    if K.shape[0] == 0:
+        return O, lse
+    S = np.where(vis, scale * (Q @ K.T), -np.inf)
+    m = np.where(vis.any(1), S.max(1), 0.0)
+    return O, lse - m
+
+
+def _attend_ignores_mask(Q, K, V, vis, scale):
+    return _orig["attend"](Q, K, V, np.ones_like(vis) & vis.any(1, keepdims=True), scale)
+
+
+def _attend_unnormalised(Q, K, V, vis, scale):
+    O, lse = _orig["attend"](Q, K, V, vis, scale)
+    if K.shape[0] == 0:
+        return O, lse
+    S = np.where(vis, scale * (Q @ K.T), -np.inf)
+    m = np.where(vis.any(1), S.max(1), 0.0)
+    l = np.where(vis, np.exp(S - m[:, None]), 0).sum(1)
+    return O * np.where(l > 0, l, 1)[:, None], lse
+
+
+def _attend_transposed_v(Q, K, V, vis, scale):
+    if V.shape[0] == V.shape[1]:
+        V = V.T
+    O, lse = _orig["attend"](Q, K, V, vis, scale)
+    return O[:, ::-1] if O.shape[1] > 1 else O, lse
+
+
+def _lengths_full_last_page(qo_indptr, kv_indptr, kv_last_page_len, page_size):
+    return _orig["request_lengths"](qo_indptr, kv_indptr, None, page_size)
+
+
+def _widen_wrong_shift(x, dtype):
+    if dtype == "bf16":
+        return (np.asarray(x).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    return np.asarray(x, np.float64)
+
+
+def _merge_no_weights(outs, lses):
+    outs = np.asarray(outs, np.float64)
+    lses = np.asarray(lses, np.float64)
+    M = lses.max(0)
+    return outs.mean(0), M
+
+
+MUTATIONS = {
+    "gather_reversed_pages": ("gather_pages", _gather_reversed_pages),
+    "gather_ignores_table": ("gather_pages", _gather_ignores_table),
+    "gather_wrong_head": ("gather_pages", _gather_wrong_head),
+    "visible_top_left": ("visible", _visible_top_left),
+    "visible_block_strict": ("visible", _visible_block_strict),
+    "visible_causal_off_by_one": ("visible", _visible_causal_off_by_one),
+    "attend_no_scale": ("attend", _attend_no_scale),
+    "attend_lse_without_max": ("attend", _attend_lse_without_max),
+    "attend_ignores_mask": ("attend", _attend_ignores_mask),
+    "attend_unnormalised": ("attend", _attend_unnormalised),
+    "attend_transposed_v": ("attend", _attend_transposed_v),
+    "lengths_full_last_page": ("request_lengths", _lengths_full_last_page),
+    "widen_wrong_shift": ("to_f64", _widen_wrong_shift),
+    "merge_no_weights": ("merge_states", _merge_no_weights),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(ref)
+        except Exception as e:  # an assertion, or a shape error from a transposed operand
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"mutation {name} passed every pin"
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in oracle_pins.ALL_PINS:
+        pin(ref)

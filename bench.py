@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Benchmark of the plan/run attention hot path on one MI355X.
+
+A step is one xattn_run over one batch of a seeded synthetic workload: every kernel
+of the run (attention, and the log-sum-exp merge when contexts are split). Plan is
+host work, done once before the timed region (its time is printed separately).
+
+Default workload: Whisper-large-style decode cross-attention (64 requests x 1 query,
+context 1500, 20 heads, head_dim 64, bf16, page_size 16, shuffled pages), metric:
+effective KV GB/s = algorithmic K+V bytes (sum of kv_len x Hkv x D x 2 x 2 B) per
+step time. Prefill workloads report TFLOP/s = 4 x D x (visible query-key pairs x Hq)
+per step time.
+
+Prints ONE JSON line. With --all, a "sweep" object carries the other workloads'
+numbers (same definitions) as well.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (prefill) and effective KV GB/s (decode) vs MI355X roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, published
+KERNEL_SOURCES = {
+    "decode": "ragged_attention_serving_amd/csrc/attn_decode.hip",
+    "mfma": "ragged_attention_serving_amd/csrc/attn_mma.hip",
+    "fp32": "ragged_attention_serving_amd/csrc/attn_f32.hip",
+    "merge": "ragged_attention_serving_amd/csrc/merge.hip",
+}
+KERNEL_NAMES = {"decode": "attn_decode_kernel", "mfma": "attn_mma_kernel", "fp32": "attn_f32_kernel",
+                "merge": "merge_kernel"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[stage], "ragged_attention_serving_amd/csrc/device.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_numbers(w, info):
+    """Algorithmic bytes and FLOPs of one step (the method's own work only)."""
+    elt = 2 if w.dtype == "bf16" else 4
+    kv_bytes = int(w.kv_lens().sum()) * w.num_kv_heads * w.head_dim * 2 * elt
+    flops = 4 * w.head_dim * int(info["visible_pairs"])
+    g = w.num_qo_heads // w.num_kv_heads
+    decode = bool(np.all(w.qo_lens() * g <= 8)) and w.dtype == "bf16"
+    return kv_bytes, flops, decode
+
+
+def to_dev(a, dtype, dev):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def measure(w, steps, warmup, dev, cold_steps=5):
+    """Plans, then times `steps` back-to-back runs (wall clock and per-kernel events)."""
+    import torch
+    import ragged_attention_serving_amd as xa
+
+    q, k, v = (to_dev(w.q, w.dtype, dev), to_dev(w.k_pages, w.dtype, dev), to_dev(w.v_pages, w.dtype, dev))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    plan = xa.Plan()
+    t0 = time.perf_counter()
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, w.num_qo_heads,
+              w.num_kv_heads, w.head_dim, w.page_size, w.num_pages, w.mask_mode, w.block_size,
+              w.sm_scale, w.dtype)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info()
+    for _ in range(warmup):
+        plan.run(q, k, v, out, lse)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` runs, synchronised on both sides
+    plan.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.run(q, k, v, out, lse)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    stages = plan.timing()
+    plan.set_timing(False)
+
+    # cold runs: 1 GiB written between runs to evict L2 and the Infinity Cache
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(cold_steps):
+        scratch.fill_(1.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        plan.run(q, k, v, out, lse)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
+    plan.close()
+    del q, k, v, out, lse
+    return dict(plan_ms=plan_ms, wall_ms=wall_ms, stages=stages, info=info,
+                cold_ms=float(np.median(cold)) if cold else None)
+
+
+def summarize(w, m):
+    kv_bytes, flops, decode = workload_numbers(w, m["info"])
+    per = {}
+    for st, (ms, n) in m["stages"].items():
+        if n:
+            per[st] = ms / n
+    dominant = max(per, key=per.get) if per else None
+    res = dict(workload=w.name, decode=decode, kv_bytes=kv_bytes, flops=flops, plan_ms=round(m["plan_ms"], 3),
+               ms_per_step=m["wall_ms"], cold_ms_per_step=m["cold_ms"],
+               kernel_ms={k: round(v, 5) for k, v in per.items()}, dominant=dominant,
+               schedule=m["info"])
+    if decode:
+        res["GBps"] = kv_bytes / (m["wall_ms"] * 1e-3) / 1e9
+        res["GBps_cold"] = kv_bytes / (m["cold_ms"] * 1e-3) / 1e9 if m["cold_ms"] else None
+        res["kernel_GBps"] = kv_bytes / (per[dominant] * 1e-3) / 1e9 if dominant else None
+        res["hbm_frac"] = res["kernel_GBps"] / HBM_PEAK_GBS if dominant else None
+    else:
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+        res["TFLOPs"] = flops / (m["wall_ms"] * 1e-3) / 1e12
+        res["TFLOPs_cold"] = flops / (m["cold_ms"] * 1e-3) / 1e12 if m["cold_ms"] else None
+        res["kernel_TFLOPs"] = flops / (per[dominant] * 1e-3) / 1e12 if dominant else None
+        res["mfma_frac"] = res["kernel_TFLOPs"] / peak if dominant else None
+        res["hbm_GBps_compulsory"] = kv_bytes / (per[dominant] * 1e-3) / 1e9 if dominant else None
+    return res
+
+
+def traffic_for(stage: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{workload}:{stage}")
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != source_sha(stage):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle as it stands, on this host, over whole passes of the workload."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import ref
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        kv_bytes = int(w.kv_lens().sum()) * w.num_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+        reqs = list(range(w.batch_size))
+        done_bytes = 0
+        done_req = 0
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < budget_s:
+            r = reqs[i % len(reqs)]
+            ref.run_workload(w, requests=[r])
+            done_bytes += int(w.kv_lens()[r]) * w.num_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+            done_req += 1
+            i += 1
+        el = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_req} request passes (all {w.num_qo_heads} heads each, {done_req / len(reqs):.2f} "
+                      f"x the workload's {len(reqs)} requests) in {el:.1f} s, one thread",
+            "workload_bytes": kv_bytes}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="whisper_decode_cross")
+    ap.add_argument("--all", action="store_true", help="also measure every other workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path is data-parallel per GPU; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ragged_attention_serving_amd import synth
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {args.workload}")
+    w = synth.WORKLOADS[args.workload](0)
+    log(f"[bench] measuring {args.workload}: steps={args.steps} warmup={args.warmup}")
+    m = measure(w, args.steps, args.warmup, dev)
+    res = summarize(w, m)
+    log(f"[bench] {json.dumps({k: v for k, v in res.items() if k != 'schedule'})}")
+
+    st = res["dominant"]
+    per_ms = res["kernel_ms"][st]
+    if res["decode"]:
+        achieved = res["kv_bytes"] / (per_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        value = res["kv_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
+        unit = "GB/s"
+    else:
+        achieved = res["flops"] / (per_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        value = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
+        unit = "TFLOP/s"
+    roof["traffic"] = traffic_for(st, w.name)
+    roof["kernel"] = KERNEL_NAMES[st]
+    roof["kernel_ms"] = round(per_ms, 5)
+    roof["kernel_source_sha"] = source_sha(st)
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.batch_size, "query_tokens": int(w.qo_indptr[-1]),
+                   "kv_tokens": int(w.kv_lens().sum()), "num_qo_heads": w.num_qo_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "mask_mode": w.mask_mode, "block_size": w.block_size, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cold_ms_per_step": round(res["cold_ms_per_step"], 5) if res["cold_ms_per_step"] else None,
+        "plan_ms": res["plan_ms"],
+        "schedule": res["schedule"],
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if args.all:
+        sweep = {}
+        for name, fn in synth.WORKLOADS.items():
+            if name == w.name:
+                continue
+            log(f"[bench] sweep: generating {name}")
+            ws = fn(0)
+            log(f"[bench] sweep: measuring {name}")
+            ms = measure(ws, max(5, min(args.steps, 20)), 3, dev)
+            r = summarize(ws, ms)
+            r.pop("schedule", None)
+            sweep[name] = r
+            log(f"[bench] {json.dumps(r)}")
+            del ws, ms
+            torch.cuda.empty_cache()
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+/*
+ * libxattn: plan/run paged attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is softmax attention of ragged, packed queries over a paged KV
+ * cache that the library only reads:
+ *
+ *  - page "mstar.engine.resources.attn.cross", FlashInferCrossManager: non-causal
+ *    paged attention over a fixed encoder context; the context is an ordinary paged
+ *    KV stream, planned once per step and run once per layer;
+ *  - same page, FlashInferCrossManager.plan: the plan result is immutable and opaque;
+ *  - same page, FlashInferCrossManager.run: one layer's attention, and nothing is
+ *    written to the context cache;
+ *  - same page, FlashInferCrossManager.force_double_buffer: a plan staged through a
+ *    reused host buffer and a non-blocking host-to-device copy races when the host
+ *    runs ahead, so the staging buffers are kept per slot and fenced before reuse;
+ *  - same page, QueryPacking: the query side is the requests in packed order plus
+ *    the cumulative query lengths (qo_indptr);
+ *  - page "mstar.engine.resources.attn.config", AttentionStep.causal: causal
+ *    self-attention over a paged cache;
+ *  - page "mstar.engine.resources.attn.ragged.base", RaggedBlockCausalAttnManager:
+ *    cacheless block-causal self-attention within each span of a packed batch;
+ *  - page "mstar.model.components.attention", Attention: grouped-query attention
+ *    when num_kv_heads < num_heads.
+ *
+ * The pages name paging but not its layout. This library reads it as a CSR page
+ * table (kv_indptr in pages, kv_page_indices, kv_last_page_len) over K and V pools
+ * laid out [num_pages][page_size][num_kv_heads][head_dim] (the per-token
+ * (len, heads, head_dim) layout of CrossAttention.compute_kv on the attention page).
+ *
+ * Conventions shared by every entry point:
+ *  - All integers are int32 unless stated; all index arrays are host memory and are
+ *    copied before the call returns (the caller may reuse them at once).
+ *  - q, out: [qo_indptr[B]][num_qo_heads][head_dim], row-major, in the plan's dtype.
+ *  - k_pages, v_pages: [num_pages][page_size][num_kv_heads][head_dim], in the plan's
+ *    dtype; they are const and never written.
+ *  - lse: [qo_indptr[B]][num_qo_heads] fp32, natural log of the softmax normaliser
+ *    of the scaled scores; -inf for a row that sees no key.
+ *  - Query row i of request r is the key position kv_len[r] - qo_len[r] + i (the
+ *    queries are the last qo_len positions of the context). CAUSAL shows it keys
+ *    j <= that position; BLOCK_CAUSAL shows it keys whose block (j / block_size) is
+ *    not after its own; NONE shows every key.
+ *  - Query head h reads KV head h / (num_qo_heads / num_kv_heads).
+ *  - Status codes: XATTN_OK (0) or a negative XATTN_ERR_*; xattn_last_error()
+ *    returns a thread-local message for the last failure.
+ *  - A handle is not thread-safe; distinct handles are independent.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define XATTN_API __attribute__((visibility("default")))
+#else
+#define XATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct xattn_plan_s* xattn_plan_t;
+
+enum xattn_mask_mode {
+  XATTN_MASK_NONE = 0,         /* cross-attention: every key */
+  XATTN_MASK_CAUSAL = 1,       /* key j <= the query's position */
+  XATTN_MASK_BLOCK_CAUSAL = 2  /* key block <= the query's block, blocks of block_size */
+};
+
+enum xattn_dtype {
+  XATTN_F32 = 0,  /* fp32 storage and arithmetic; head_dim in {16, 32, 64, 128} */
+  XATTN_BF16 = 1  /* bf16 storage, fp32 accumulation; head_dim in {64, 128} */
+};
+
+enum xattn_status {
+  XATTN_OK = 0,
+  XATTN_ERR_INVALID_ARG = -1, /* an argument breaks the contract above */
+  XATTN_ERR_UNSUPPORTED = -2, /* valid but not built (e.g. head_dim) */
+  XATTN_ERR_HIP = -3,         /* a HIP runtime call failed */
+  XATTN_ERR_OOM = -4,         /* device or pinned host allocation failed */
+  XATTN_ERR_BUSY = -5         /* reserved: the slot to be planned is still in use */
+};
+
+/*
+ * xattn_plan: validate the page table and query packing, partition the work into
+ * units (splitting long contexts into KV chunks whose partial results are merged
+ * on the log-sum-exp), and stage the schedule for xattn_run.
+ *
+ * plan            in/out. *plan == NULL creates a handle; otherwise the new schedule
+ *                 is written into the handle's other slot (two slots: pinned host
+ *                 staging + device copy + fp32 split workspace each). Before a slot is
+ *                 rewritten the call waits on that slot's fence, which covers its
+ *                 host-to-device copy and every run that read it.
+ * qo_indptr       [batch_size + 1]; qo_indptr[0] == 0, non-decreasing.
+ * kv_indptr       [batch_size + 1]; page counts; kv_indptr[0] == 0, non-decreasing.
+ * kv_page_indices [kv_indptr[batch_size]], each in [0, num_pages); NULL means the
+ *                 identity table (logical page p of the batch is physical page p), which
+ *                 is how cacheless spans are passed: page_size 1, kv_indptr equal to
+ *                 the spans' cu_seqlens, and k_pages the packed keys [T][1][H][D].
+ * kv_last_page_len [batch_size], each in [1, page_size] for a request with pages;
+ *                 NULL means every last page is full.
+ * batch_size      number of requests B >= 0.
+ * num_qo_heads, num_kv_heads  >= 1, num_qo_heads % num_kv_heads == 0.
+ * head_dim        see xattn_dtype.
+ * page_size       tokens per page, >= 1.
+ * num_pages       pages in the K and V pools; every referenced page must lie below it.
+ * mask_mode       an xattn_mask_mode. CAUSAL and BLOCK_CAUSAL need qo_len <= kv_len.
+ * block_size      >= 1, read only for BLOCK_CAUSAL.
+ * sm_scale        score scale; <= 0 means 1 / sqrt(head_dim).
+ * dtype           an xattn_dtype.
+ * stream          hipStream_t for the host-to-device copy (NULL: the null stream).
+ *
+ * On error the handle (if any) keeps its previous schedule unchanged.
+ */
+XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+               const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+               int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
+               int32_t block_size, float sm_scale, int32_t dtype, void* stream);
+
+/*
+ * xattn_run: one layer's attention with the latest schedule (page
+ * "mstar.engine.resources.attn.cross", FlashInferCrossManager.run). Launches the
+ * attention kernels, and the log-sum-exp merge kernel when a context was split, on
+ * `stream`, then records the slot's fence there. Any number of runs (one per layer,
+ * each with its own q/k/v/out) may share one plan.
+ *
+ * q, k_pages, v_pages  device pointers, layouts above, 16-byte aligned; k_pages and
+ *                      v_pages are not written.
+ * out                  device pointer, caller-allocated, 16-byte aligned.
+ * lse                  device pointer (4-byte aligned) or NULL (not written).
+ * stream               hipStream_t (NULL: the null stream).
+ *
+ * Returns XATTN_ERR_INVALID_ARG for a handle with no schedule, a NULL pointer that
+ * the schedule needs or a misaligned pointer, XATTN_ERR_HIP for a launch failure. Device faults
+ * surface at the caller's next synchronisation. Pointers are borrowed until the
+ * stream passes the run.
+ */
+XATTN_API int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+              void* out, float* lse, void* stream);
+
+/* 1 if the next xattn_plan on this handle would not wait on a fence, 0 if it would,
+ * negative on error. Never blocks. */
+XATTN_API int xattn_plan_ready(xattn_plan_t plan);
+
+/* Waits on both slot fences, then frees the handle. NULL is ignored. */
+XATTN_API void xattn_plan_destroy(xattn_plan_t plan);
+
+/* Thread-local message for the last non-OK status of this thread ("" if none). */
+XATTN_API const char* xattn_last_error(void);
+
+/* What a schedule holds (host-side summary, no GPU involved). */
+typedef struct xattn_schedule_info {
+  int32_t num_units[3];     /* per kernel family: 0 fp32, 1 bf16 decode, 2 bf16 MFMA tile */
+  int32_t chunk_tokens[3];  /* KV chunk length per family (0: family unused) */
+  int32_t decode_rows;      /* query rows (tokens x grouped heads) per decode unit */
+  int32_t num_merge_rows;   /* output rows assembled from split chunks */
+  int64_t workspace_rows;   /* fp32 partial rows (head_dim values + 1 lse each) */
+  int64_t total_kv_tokens;  /* sum over requests of kv_len */
+  int64_t visible_pairs;    /* sum over query rows and heads of visible keys */
+} xattn_schedule_info;
+
+/*
+ * xattn_schedule: build, on the host only, the schedule xattn_plan would stage for
+ * the same arguments (no GPU call, usable without a device). Fills *info. When
+ * `units` is not NULL it receives sum(num_units) records of 8 int32 each, families in
+ * order: {request, kv_head, row0, nrows, kv_begin, kv_end, workspace_row (-1: written
+ * straight to out), cost}. Query row `row` of a request is token row / group of head
+ * kv_head * group + row % group. When `merges` is not NULL it receives num_merge_rows
+ * records of 4 int32: {out_row = token * num_qo_heads + head, first workspace row,
+ * chunk count, workspace row stride between chunks}. Same errors as xattn_plan.
+ */
+XATTN_API int xattn_schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                   const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                   int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
+                   int32_t block_size, int32_t dtype, int32_t force_chunk,
+                   xattn_schedule_info* info, int32_t* units, int32_t* merges);
+
+/* The summary of the handle's current schedule. */
+XATTN_API int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info);
+
+/*
+ * Kernel timing. With enable != 0, every later xattn_run on this handle records a pair
+ * of HIP events around each kernel it launches, on the run's stream (at most 65536
+ * pairs are kept; later runs are not recorded until the next collection).
+ * xattn_plan_timing waits for the recorded events, writes the summed milliseconds
+ * and the launch count per stage {0 fp32, 1 bf16 decode, 2 bf16 MFMA tile, 3 merge}
+ * into ms[4] and launches[4], and clears the records. enable == 0 stops recording.
+ */
+XATTN_API int xattn_plan_set_timing(xattn_plan_t plan, int enable);
+XATTN_API int xattn_plan_timing(xattn_plan_t plan, double* ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

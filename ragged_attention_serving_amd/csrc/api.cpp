@@ -1,0 +1,443 @@
+// libxattn C ABI: plan (host schedule, double-buffered staging) and run (launches).
+//
+// Double buffering follows page "mstar.engine.resources.attn.cross",
+// FlashInferCrossManager.force_double_buffer: a plan is staged in a pinned host
+// buffer and copied to the device with a non-blocking copy, so planning step N+1
+// into the same buffer before step N's copy (and the runs that read it) retired would
+// race. Each handle therefore owns two slots; plan N writes slot N % 2 after waiting
+// on that slot's fence, and run reads the latest slot and re-arms its fence.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/xattn.h"
+#include "kernels.h"
+#include "partition.h"
+
+using xattn::AttnParams;
+using xattn::Schedule;
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_err(hipError_t e, const char* what) {
+  return set_err(XATTN_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  return s && *s ? std::atoi(s) : dflt;
+}
+
+size_t align_words(size_t n) { return (n + 63) & ~static_cast<size_t>(63); }
+
+constexpr size_t kMaxTimingRecs = 65536;
+
+struct Slot {
+  void* host = nullptr;  // pinned staging
+  size_t host_cap = 0;
+  void* dev = nullptr;
+  size_t dev_cap = 0;
+  float* ws = nullptr;  // [ws_rows][d] partial O, then [ws_rows] partial lse
+  size_t ws_cap = 0;    // bytes
+  hipEvent_t fence = nullptr;     // covers the slot's copy and every run that read it
+  hipEvent_t uploaded = nullptr;  // the slot's host-to-device copy
+  bool fenced = false;
+  bool ready = false;
+  // schedule summary and device offsets (in int32 words from dev)
+  Schedule sched;
+  size_t off_reqs = 0, off_units[xattn::FAM_COUNT] = {0, 0, 0}, off_merges = 0, off_pages = 0;
+  int32_t dtype = 0, hq = 0, hkv = 0, d = 0, page_size = 0, mask = 0, block = 0;
+};
+
+}  // namespace
+
+struct TimingRec {
+  int stage;
+  hipEvent_t start, stop;
+};
+
+struct xattn_plan_s {
+  Slot slot[2];
+  int cur = -1;
+  int device = 0;
+  bool timing = false;
+  std::vector<hipEvent_t> event_pool;
+  std::vector<TimingRec> timing_recs;
+};
+
+namespace {
+
+int ensure(void** ptr, size_t* cap, size_t need, bool pinned) {
+  if (*cap >= need && *ptr) return XATTN_OK;
+  size_t want = need < 4096 ? 4096 : need + need / 4;
+  if (*ptr) {
+    hipError_t e = pinned ? hipHostFree(*ptr) : hipFree(*ptr);
+    *ptr = nullptr;
+    *cap = 0;
+    if (e != hipSuccess) return hip_err(e, "free");
+  }
+  hipError_t e = pinned ? hipHostMalloc(ptr, want, hipHostMallocDefault) : hipMalloc(ptr, want);
+  if (e != hipSuccess) {
+    *ptr = nullptr;
+    (void)hipGetLastError();
+    return set_err(XATTN_ERR_OOM, std::string(pinned ? "hipHostMalloc" : "hipMalloc") + " failed: " +
+                                      hipGetErrorString(e));
+  }
+  *cap = want;
+  return XATTN_OK;
+}
+
+void log_schedule(const Schedule& s) {
+  std::fprintf(stderr,
+               "[xattn] plan: units f32=%zu dec=%zu (rows %d) mma=%zu; chunks %d/%d/%d; "
+               "merge rows %zu; workspace rows %lld; kv tokens %lld\n",
+               s.units[0].size(), s.units[1].size(), s.dec_rows, s.units[2].size(), s.chunk[0],
+               s.chunk[1], s.chunk[2], s.merges.size(), static_cast<long long>(s.ws_rows),
+               static_cast<long long>(s.total_kv));
+}
+
+void fill_info(const Schedule& s, xattn_schedule_info* info) {
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) {
+    info->num_units[f] = static_cast<int32_t>(s.units[f].size());
+    info->chunk_tokens[f] = s.units[f].empty() ? 0 : s.chunk[f];
+  }
+  info->decode_rows = s.dec_rows;
+  info->num_merge_rows = static_cast<int32_t>(s.merges.size());
+  info->workspace_rows = s.ws_rows;
+  info->total_kv_tokens = s.total_kv;
+  info->visible_pairs = s.visible_pairs;
+}
+
+xattn::PlanArgs make_args(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                          int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
+                          int32_t block_size, float sm_scale, int32_t dtype, int32_t force_chunk) {
+  xattn::PlanArgs a;
+  a.qo_indptr = qo_indptr;
+  a.kv_indptr = kv_indptr;
+  a.kv_page_indices = kv_page_indices;
+  a.kv_last_page_len = kv_last_page_len;
+  a.batch = batch_size;
+  a.hq = num_qo_heads;
+  a.hkv = num_kv_heads;
+  a.d = head_dim;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.mask = mask_mode;
+  a.block = block_size;
+  a.sm_scale = sm_scale;
+  a.dtype = dtype;
+  a.force_chunk = force_chunk;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xattn_last_error(void) { return g_err.c_str(); }
+
+int xattn_schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                   const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+                   int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
+                   int32_t block_size, int32_t dtype, int32_t force_chunk,
+                   xattn_schedule_info* info, int32_t* units, int32_t* merges) {
+  if (!info) return set_err(XATTN_ERR_INVALID_ARG, "info is NULL");
+  Schedule s;
+  std::string err;
+  const xattn::PlanArgs a = make_args(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len,
+                                      batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                      num_pages, mask_mode, block_size, 0.f, dtype, force_chunk);
+  const int rc = xattn::build_schedule(a, s, err);
+  if (rc != XATTN_OK) return set_err(rc, err);
+  fill_info(s, info);
+  if (units) {
+    int32_t* dst = units;
+    for (int f = 0; f < xattn::FAM_COUNT; ++f) {
+      std::memcpy(dst, s.units[f].data(), s.units[f].size() * sizeof(xattn::Unit));
+      dst += s.units[f].size() * 8;
+    }
+  }
+  if (merges) std::memcpy(merges, s.merges.data(), s.merges.size() * sizeof(xattn::Merge));
+  return XATTN_OK;
+}
+
+int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+               const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+               int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
+               int32_t block_size, float sm_scale, int32_t dtype, void* stream) {
+  if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
+  Schedule s;
+  std::string err;
+  const xattn::PlanArgs a =
+      make_args(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size, num_qo_heads,
+                num_kv_heads, head_dim, page_size, num_pages, mask_mode, block_size, sm_scale, dtype,
+                env_int("XATTN_FORCE_CHUNK", 0));
+  const int rc = xattn::build_schedule(a, s, err);
+  if (rc != XATTN_OK) return set_err(rc, err);
+  if (env_int("XATTN_LOG", 0)) log_schedule(s);
+
+  bool created = false;
+  if (*plan == nullptr) {
+    *plan = new xattn_plan_s();
+    created = true;
+    (void)hipGetDevice(&(*plan)->device);
+  }
+  xattn_plan_s* h = *plan;
+  auto fail = [&](int code) {
+    if (created) {
+      xattn_plan_destroy(h);
+      *plan = nullptr;
+    }
+    return code;
+  };
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev != h->device) return fail(set_err(XATTN_ERR_INVALID_ARG, "plan used on another device"));
+
+  const int si = h->cur < 0 ? 0 : (h->cur ^ 1);
+  Slot& sl = h->slot[si];
+  hipError_t e;
+  if (!sl.fence) {
+    if ((e = hipEventCreateWithFlags(&sl.fence, hipEventDisableTiming)) != hipSuccess)
+      return fail(hip_err(e, "hipEventCreate"));
+    if ((e = hipEventCreateWithFlags(&sl.uploaded, hipEventDisableTiming)) != hipSuccess)
+      return fail(hip_err(e, "hipEventCreate"));
+  }
+  if (sl.fenced) {
+    // the slot's previous copy and every run that read it must retire before reuse
+    if ((e = hipEventSynchronize(sl.fence)) != hipSuccess) return fail(hip_err(e, "hipEventSynchronize"));
+  }
+
+  // device image: reqs | units per family | merges | page indices (int32 words)
+  size_t words = 0;
+  const size_t off_reqs = words;
+  words = align_words(words + s.reqs.size());
+  size_t off_units[xattn::FAM_COUNT];
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) {
+    off_units[f] = words;
+    words = align_words(words + s.units[f].size() * 8);
+  }
+  const size_t off_merges = words;
+  words = align_words(words + s.merges.size() * 4);
+  const size_t off_pages = words;
+  words = align_words(words + s.pages.size());
+  const size_t bytes = words * sizeof(int32_t);
+
+  int st;
+  if ((st = ensure(&sl.host, &sl.host_cap, bytes, true)) != XATTN_OK) return fail(st);
+  if ((st = ensure(&sl.dev, &sl.dev_cap, bytes, false)) != XATTN_OK) return fail(st);
+  const size_t ws_bytes = static_cast<size_t>(s.ws_rows) * (head_dim + 1) * sizeof(float);
+  if (ws_bytes > 0) {
+    void* w = sl.ws;
+    if ((st = ensure(&w, &sl.ws_cap, ws_bytes, false)) != XATTN_OK) {
+      sl.ws = nullptr;
+      return fail(st);
+    }
+    sl.ws = static_cast<float*>(w);
+  }
+
+  int32_t* img = static_cast<int32_t*>(sl.host);
+  std::memcpy(img + off_reqs, s.reqs.data(), s.reqs.size() * sizeof(int32_t));
+  for (int f = 0; f < xattn::FAM_COUNT; ++f)
+    std::memcpy(img + off_units[f], s.units[f].data(), s.units[f].size() * sizeof(xattn::Unit));
+  std::memcpy(img + off_merges, s.merges.data(), s.merges.size() * sizeof(xattn::Merge));
+  std::memcpy(img + off_pages, s.pages.data(), s.pages.size() * sizeof(int32_t));
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  if ((e = hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, strm)) != hipSuccess)
+    return fail(hip_err(e, "hipMemcpyAsync"));
+  if ((e = hipEventRecord(sl.uploaded, strm)) != hipSuccess) return fail(hip_err(e, "hipEventRecord"));
+  if ((e = hipEventRecord(sl.fence, strm)) != hipSuccess) return fail(hip_err(e, "hipEventRecord"));
+  sl.fenced = true;
+
+  sl.off_reqs = off_reqs;
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) sl.off_units[f] = off_units[f];
+  sl.off_merges = off_merges;
+  sl.off_pages = off_pages;
+  sl.dtype = dtype;
+  sl.hq = num_qo_heads;
+  sl.hkv = num_kv_heads;
+  sl.d = head_dim;
+  sl.page_size = page_size;
+  sl.mask = mask_mode;
+  sl.block = block_size;
+  sl.sched = std::move(s);
+  sl.ready = true;
+  h->cur = si;
+  return XATTN_OK;
+}
+
+int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages, void* out,
+              float* lse, void* stream) {
+  if (!plan || plan->cur < 0 || !plan->slot[plan->cur].ready)
+    return set_err(XATTN_ERR_INVALID_ARG, "run without a successful plan");
+  Slot& sl = plan->slot[plan->cur];
+  const Schedule& s = sl.sched;
+  size_t nunits = 0;
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) nunits += s.units[f].size();
+  if (nunits > 0 && (!q || !out)) return set_err(XATTN_ERR_INVALID_ARG, "q and out are required");
+  if (s.total_kv > 0 && (!k_pages || !v_pages))
+    return set_err(XATTN_ERR_INVALID_ARG, "k_pages and v_pages are required");
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) |
+                        reinterpret_cast<uintptr_t>(v_pages) | reinterpret_cast<uintptr_t>(out);
+  if (mis & 15) return set_err(XATTN_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3) return set_err(XATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = hipStreamWaitEvent(strm, sl.uploaded, 0)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+
+  const int32_t* dev = static_cast<const int32_t*>(sl.dev);
+  AttnParams p{};
+  p.q = q;
+  p.k = k_pages;
+  p.v = v_pages;
+  p.out = out;
+  p.lse = lse;
+  p.ws_o = sl.ws;
+  p.ws_lse = sl.ws ? sl.ws + static_cast<size_t>(s.ws_rows) * sl.d : nullptr;
+  p.reqs = dev + sl.off_reqs;
+  p.pages = s.identity ? nullptr : dev + sl.off_pages;
+  p.merges = dev + sl.off_merges;
+  p.num_merges = static_cast<int32_t>(s.merges.size());
+  p.hq = sl.hq;
+  p.hkv = sl.hkv;
+  p.d = sl.d;
+  p.group = s.group;
+  p.page_size = sl.page_size;
+  p.page_shift = -1;
+  if ((sl.page_size & (sl.page_size - 1)) == 0) {
+    int sh = 0;
+    while ((1 << sh) < sl.page_size) ++sh;
+    p.page_shift = sh;
+  }
+  p.mask = sl.mask;
+  p.block = sl.mask == 2 ? sl.block : 1;
+  p.scale = s.scale;
+  p.scale_log2 = s.scale * 1.4426950408889634f;
+
+  // optional per-kernel events (xattn_plan_set_timing)
+  const bool timed = plan->timing && plan->timing_recs.size() < kMaxTimingRecs;
+  auto event = [&](hipEvent_t* ev) -> hipError_t {
+    if (!plan->event_pool.empty()) {
+      *ev = plan->event_pool.back();
+      plan->event_pool.pop_back();
+      return hipSuccess;
+    }
+    return hipEventCreate(ev);
+  };
+  TimingRec rec{};
+  auto begin = [&](int stage) -> hipError_t {
+    if (!timed) return hipSuccess;
+    rec.stage = stage;
+    hipError_t r = event(&rec.start);
+    if (r == hipSuccess) r = event(&rec.stop);
+    if (r == hipSuccess) r = hipEventRecord(rec.start, strm);
+    return r;
+  };
+  auto end = [&]() -> hipError_t {
+    if (!timed) return hipSuccess;
+    const hipError_t r = hipEventRecord(rec.stop, strm);
+    if (r == hipSuccess) plan->timing_recs.push_back(rec);
+    return r;
+  };
+
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) {
+    if (s.units[f].empty()) continue;
+    p.units = dev + sl.off_units[f];
+    p.num_units = static_cast<int32_t>(s.units[f].size());
+    if ((e = begin(f)) != hipSuccess) return hip_err(e, "timing event");
+    if (f == xattn::FAM_F32) e = xattn::launch_attn_f32(p, strm);
+    else if (f == xattn::FAM_DEC) e = xattn::launch_attn_decode(p, s.dec_rows, strm);
+    else e = xattn::launch_attn_mma(p, strm);
+    if (e != hipSuccess) return hip_err(e, "attention kernel launch");
+    if ((e = end()) != hipSuccess) return hip_err(e, "timing event");
+  }
+  if (!s.merges.empty()) {
+    if ((e = begin(3)) != hipSuccess) return hip_err(e, "timing event");
+    if ((e = xattn::launch_merge(p, sl.dtype, strm)) != hipSuccess) return hip_err(e, "merge kernel launch");
+    if ((e = end()) != hipSuccess) return hip_err(e, "timing event");
+  }
+  if ((e = hipEventRecord(sl.fence, strm)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  return XATTN_OK;
+}
+
+int xattn_plan_ready(xattn_plan_t plan) {
+  if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
+  const Slot& sl = plan->slot[plan->cur < 0 ? 0 : (plan->cur ^ 1)];
+  if (!sl.fenced) return 1;
+  const hipError_t e = hipEventQuery(sl.fence);
+  if (e == hipSuccess) return 1;
+  if (e == hipErrorNotReady) return 0;
+  return hip_err(e, "hipEventQuery");
+}
+
+int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info) {
+  if (!plan || !info) return set_err(XATTN_ERR_INVALID_ARG, "NULL argument");
+  if (plan->cur < 0) return set_err(XATTN_ERR_INVALID_ARG, "no schedule yet");
+  fill_info(plan->slot[plan->cur].sched, info);
+  return XATTN_OK;
+}
+
+int xattn_plan_set_timing(xattn_plan_t plan, int enable) {
+  if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
+  plan->timing = enable != 0;
+  return XATTN_OK;
+}
+
+int xattn_plan_timing(xattn_plan_t plan, double* ms, int32_t* launches) {
+  if (!plan || !ms || !launches) return set_err(XATTN_ERR_INVALID_ARG, "NULL argument");
+  for (int i = 0; i < 4; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  int rc = XATTN_OK;
+  for (const TimingRec& r : plan->timing_recs) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess && rc == XATTN_OK) rc = hip_err(e, "hipEventElapsedTime");
+    ms[r.stage] += t;
+    launches[r.stage] += 1;
+    plan->event_pool.push_back(r.start);
+    plan->event_pool.push_back(r.stop);
+  }
+  plan->timing_recs.clear();
+  return rc;
+}
+
+void xattn_plan_destroy(xattn_plan_t plan) {
+  if (!plan) return;
+  for (const TimingRec& r : plan->timing_recs) {
+    (void)hipEventSynchronize(r.stop);
+    plan->event_pool.push_back(r.start);
+    plan->event_pool.push_back(r.stop);
+  }
+  for (hipEvent_t ev : plan->event_pool) (void)hipEventDestroy(ev);
+  for (Slot& sl : plan->slot) {
+    if (sl.fenced && sl.fence) (void)hipEventSynchronize(sl.fence);
+    if (sl.fence) (void)hipEventDestroy(sl.fence);
+    if (sl.uploaded) (void)hipEventDestroy(sl.uploaded);
+    if (sl.host) (void)hipHostFree(sl.host);
+    if (sl.dev) (void)hipFree(sl.dev);
+    if (sl.ws) (void)hipFree(sl.ws);
+  }
+  delete plan;
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Kernel argument block shared by the run-side launcher (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace xattn {
+
+struct AttnParams {
+  const void* q;        // [total_q][hq][d]
+  const void* k;        // [num_pages][page_size][hkv][d]
+  const void* v;        // same layout as k
+  void* out;            // [total_q][hq][d]
+  float* lse;           // [total_q][hq] or nullptr
+  float* ws_o;          // [ws_rows][d] fp32 partial outputs (normalised)
+  float* ws_lse;        // [ws_rows] fp32 partial lse (natural log)
+  const int32_t* reqs;  // [B][4]: qo_start, qo_len, kv_len, page_base
+  const int32_t* units; // [n][8]: r, hk, row0, nrows, kv0, kv1, ws_row, cost
+  const int32_t* pages; // [total_pages] physical page per logical page; nullptr: identity
+  const int32_t* merges;// [m][4]: out_row, ws_row0, nchunks, stride
+  int32_t num_units;
+  int32_t num_merges;
+  int32_t hq, hkv, d, group;
+  int32_t page_size;
+  int32_t page_shift;   // log2(page_size) when a power of two, else -1
+  int32_t mask, block;
+  float scale;          // softmax scale
+  float scale_log2;     // scale * log2(e)
+};
+
+}  // namespace xattn

@@ -1,0 +1,241 @@
+// Host-side schedule: validation, partition into units, KV chunking and merge map.
+//
+// Inputs follow the query packing of page "mstar.engine.resources.attn.cross"
+// (QueryPacking: requests in packed order plus cumulative query lengths) and a CSR
+// page table over the context (FlashInferCrossManager reads the context as an
+// ordinary paged KV stream). Long contexts are split into KV chunks spread across
+// compute units; split rows are put back together by a log-sum-exp merge.
+#include "partition.h"
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <numeric>
+
+namespace xattn {
+
+int64_t last_visible_key(int mask, int block, int64_t qo_len, int64_t kv_len, int64_t qi) {
+  if (kv_len <= 0) return -1;
+  const int64_t pos = kv_len - qo_len + qi;  // this query's key position
+  switch (mask) {
+    case 0:
+      return kv_len - 1;
+    case 1:
+      return std::min(pos, kv_len - 1);
+    default: {
+      const int64_t end = (pos / block + 1) * block;  // first key of the next block
+      return std::min(end, kv_len) - 1;
+    }
+  }
+}
+
+static int fail(std::string& err, int code, const std::string& msg) {
+  err = msg;
+  return code;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
+  s = Schedule();
+  const int B = a.batch;
+  if (B < 0) return fail(err, kErrInvalid, "batch_size < 0");
+  if (B > 0 && (!a.qo_indptr || !a.kv_indptr))
+    return fail(err, kErrInvalid, "qo_indptr and kv_indptr are required");
+  if (a.hq < 1 || a.hkv < 1) return fail(err, kErrInvalid, "head counts must be >= 1");
+  if (a.hq % a.hkv != 0) return fail(err, kErrInvalid, "num_qo_heads % num_kv_heads != 0");
+  if (a.page_size < 1) return fail(err, kErrInvalid, "page_size < 1");
+  if (a.mask < 0 || a.mask > 2) return fail(err, kErrInvalid, "unknown mask_mode");
+  if (a.mask == 2 && a.block < 1) return fail(err, kErrInvalid, "block_size < 1 for BLOCK_CAUSAL");
+  if (a.dtype != 0 && a.dtype != 1) return fail(err, kErrInvalid, "unknown dtype");
+  if (a.dtype == 0 && a.d != 16 && a.d != 32 && a.d != 64 && a.d != 128)
+    return fail(err, kErrUnsupported, "fp32 head_dim must be 16, 32, 64 or 128");
+  if (a.dtype == 1 && a.d != 64 && a.d != 128)
+    return fail(err, kErrUnsupported, "bf16 head_dim must be 64 or 128");
+  if (a.force_chunk < 0) return fail(err, kErrInvalid, "force_chunk < 0");
+
+  const int g = a.hq / a.hkv;
+  s.group = g;
+  s.scale = a.sm_scale > 0.f ? a.sm_scale : 1.0f / std::sqrt(static_cast<float>(a.d));
+  s.identity = a.kv_page_indices == nullptr;
+
+  // ---- validate the packing and the page table, collect per-request lengths
+  if (B > 0 && (a.qo_indptr[0] != 0 || a.kv_indptr[0] != 0))
+    return fail(err, kErrInvalid, "qo_indptr[0] and kv_indptr[0] must be 0");
+  s.reqs.resize(static_cast<size_t>(B) * 4);
+  for (int r = 0; r < B; ++r) {
+    const int64_t qo = static_cast<int64_t>(a.qo_indptr[r + 1]) - a.qo_indptr[r];
+    const int64_t np = static_cast<int64_t>(a.kv_indptr[r + 1]) - a.kv_indptr[r];
+    if (qo < 0) return fail(err, kErrInvalid, "qo_indptr decreases at request " + std::to_string(r));
+    if (np < 0) return fail(err, kErrInvalid, "kv_indptr decreases at request " + std::to_string(r));
+    int64_t kv = 0;
+    if (np > 0) {
+      int64_t last = a.page_size;
+      if (a.kv_last_page_len) {
+        last = a.kv_last_page_len[r];
+        if (last < 1 || last > a.page_size)
+          return fail(err, kErrInvalid,
+                      "kv_last_page_len out of [1, page_size] at request " + std::to_string(r));
+      }
+      kv = (np - 1) * a.page_size + last;
+      if (kv > INT32_MAX) return fail(err, kErrInvalid, "context longer than 2^31-1 keys");
+    }
+    if (a.mask != 0 && qo > kv)
+      return fail(err, kErrInvalid,
+                  "causal masks need qo_len <= kv_len (request " + std::to_string(r) + ")");
+    s.reqs[4 * r + 0] = a.qo_indptr[r];
+    s.reqs[4 * r + 1] = static_cast<int32_t>(qo);
+    s.reqs[4 * r + 2] = static_cast<int32_t>(kv);
+    s.reqs[4 * r + 3] = a.kv_indptr[r];
+    s.total_kv += kv;
+  }
+  s.total_q = B > 0 ? a.qo_indptr[B] : 0;
+  if (static_cast<int64_t>(s.total_q) * a.hq > INT32_MAX)
+    return fail(err, kErrInvalid, "too many query rows");
+  const int64_t total_pages = B > 0 ? a.kv_indptr[B] : 0;
+  if (total_pages > 0 && a.num_pages < 1) return fail(err, kErrInvalid, "num_pages is required");
+  if (s.identity) {
+    if (total_pages > a.num_pages && total_pages > 0)
+      return fail(err, kErrInvalid, "identity page table runs past num_pages");
+  } else if (total_pages > 0) {
+    s.pages.assign(a.kv_page_indices, a.kv_page_indices + total_pages);
+    for (int64_t i = 0; i < total_pages; ++i) {
+      const int32_t p = s.pages[i];
+      if (p < 0 || p >= a.num_pages)
+        return fail(err, kErrInvalid, "kv_page_indices[" + std::to_string(i) + "] out of range");
+    }
+  }
+
+  // ---- classify requests and size the work per family
+  auto family_of = [&](int64_t rows) -> int {
+    if (a.dtype == 0) return FAM_F32;
+    return rows <= kDecMaxRows ? FAM_DEC : FAM_MMA;
+  };
+  auto rows_per_unit = [&](int fam) -> int64_t {
+    return fam == FAM_F32 ? kF32Rows : fam == FAM_DEC ? kDecMaxRows : kMmaRows;
+  };
+  // KV range [0, hi) a row tile needs: up to the last key its last row sees.
+  auto tile_hi = [&](int r, int64_t row_end) -> int64_t {
+    const int64_t qo = s.reqs[4 * r + 1], kv = s.reqs[4 * r + 2];
+    const int64_t qi_max = (row_end - 1) / g;
+    return last_visible_key(a.mask, a.block, qo, kv, qi_max) + 1;
+  };
+
+  int64_t fam_work[FAM_COUNT] = {0, 0, 0};   // key-heads (decode) or tile count (mma)
+  int64_t fam_maxkv[FAM_COUNT] = {0, 0, 0};
+  int dec_rows = 0;
+  for (int r = 0; r < B; ++r) {
+    const int64_t qo = s.reqs[4 * r + 1];
+    if (qo == 0) continue;
+    const int64_t rows = qo * g;
+    const int fam = family_of(rows);
+    const int64_t rpu = rows_per_unit(fam);
+    if (fam == FAM_DEC) dec_rows = std::max<int>(dec_rows, static_cast<int>(rows));
+    for (int64_t row0 = 0; row0 < rows; row0 += rpu) {
+      const int64_t row_end = std::min(rows, row0 + rpu);
+      const int64_t hi = tile_hi(r, row_end);
+      fam_work[fam] += (fam == FAM_MMA ? 1 : hi) * a.hkv;
+      fam_maxkv[fam] = std::max(fam_maxkv[fam], hi);
+    }
+    // visible pairs: exact count per query row, for the metric
+    const int64_t kv = s.reqs[4 * r + 2];
+    for (int64_t qi = 0; qi < qo; ++qi)
+      s.visible_pairs += (last_visible_key(a.mask, a.block, qo, kv, qi) + 1) * a.hq;
+  }
+  if (dec_rows > 0) {
+    int R = 1;
+    while (R < dec_rows) R *= 2;
+    s.dec_rows = R;
+  }
+
+  // chunk length per family
+  int64_t chunk[FAM_COUNT] = {0, 0, 0};
+  for (int fam = 0; fam < FAM_COUNT; ++fam) {
+    if (fam_maxkv[fam] == 0 && fam_work[fam] == 0) continue;
+    int64_t c;
+    if (a.force_chunk > 0) {
+      c = a.force_chunk;
+    } else if (fam == FAM_F32) {
+      c = kF32MaxChunk;
+    } else if (fam == FAM_DEC) {
+      // about 2048 units of at least 256 keys: several waves of work per compute unit
+      c = std::max<int64_t>(256, round_up(ceil_div(std::max<int64_t>(fam_work[fam], 1), 2048), 64));
+    } else {
+      // split only when there are too few query tiles to fill 256 compute units twice
+      const int64_t tiles = std::max<int64_t>(fam_work[fam], 1);
+      if (tiles >= 512) {
+        c = std::max<int64_t>(fam_maxkv[fam], 1);
+      } else {
+        const int64_t f = ceil_div(512, tiles);
+        c = std::max<int64_t>(256, round_up(ceil_div(fam_maxkv[fam], f), 64));
+      }
+    }
+    if (fam == FAM_F32) c = std::min<int64_t>(c, kF32MaxChunk);
+    c = std::min<int64_t>(std::max<int64_t>(c, 1), INT32_MAX);
+    chunk[fam] = c;
+    s.chunk[fam] = static_cast<int32_t>(c);
+  }
+
+  // ---- emit units and the merge map
+  for (int r = 0; r < B; ++r) {
+    const int64_t qo = s.reqs[4 * r + 1];
+    if (qo == 0) continue;
+    const int64_t qo_start = s.reqs[4 * r + 0];
+    const int64_t rows = qo * g;
+    const int fam = family_of(rows);
+    const int64_t rpu = rows_per_unit(fam);
+    for (int hk = 0; hk < a.hkv; ++hk) {
+      for (int64_t row0 = 0; row0 < rows; row0 += rpu) {
+        const int64_t row_end = std::min(rows, row0 + rpu);
+        const int64_t nrows = row_end - row0;
+        const int64_t hi = tile_hi(r, row_end);
+        const int64_t nch = hi <= 0 ? 1 : ceil_div(hi, chunk[fam]);
+        // equal chunks, rounded to whole 64-key tiles when that keeps the count; a forced
+        // chunk length is taken as given
+        int64_t step = hi <= 0 ? 1 : ceil_div(hi, nch);
+        if (a.force_chunk > 0) step = chunk[fam];
+        else if (nch > 1 && ceil_div(hi, round_up(step, 64)) == nch) step = round_up(step, 64);
+        int32_t base = -1;
+        if (nch > 1) {
+          if (s.ws_rows + nch * nrows > INT32_MAX) return fail(err, kErrInvalid, "workspace too large");
+          base = static_cast<int32_t>(s.ws_rows);
+          s.ws_rows += nch * nrows;
+          for (int64_t rr = 0; rr < nrows; ++rr) {
+            const int64_t row = row0 + rr;
+            const int64_t tok = qo_start + row / g;
+            const int64_t head = static_cast<int64_t>(hk) * g + row % g;
+            s.merges.push_back(Merge{static_cast<int32_t>(tok * a.hq + head),
+                                     static_cast<int32_t>(base + rr), static_cast<int32_t>(nch),
+                                     static_cast<int32_t>(nrows)});
+          }
+        }
+        for (int64_t c = 0; c < nch; ++c) {
+          const int64_t k0 = hi <= 0 ? 0 : std::min(hi, c * step);
+          const int64_t k1 = hi <= 0 ? 0 : std::min(hi, (c + 1) * step);
+          Unit u;
+          u.r = r;
+          u.hk = hk;
+          u.row0 = static_cast<int32_t>(row0);
+          u.nrows = static_cast<int32_t>(nrows);
+          u.kv0 = static_cast<int32_t>(k0);
+          u.kv1 = static_cast<int32_t>(k1);
+          u.ws_row = nch > 1 ? static_cast<int32_t>(base + c * nrows) : -1;
+          const int64_t cost = (k1 - k0 + 64) * (fam == FAM_MMA ? (nrows + 31) / 32 : 1);
+          u.cost = static_cast<int32_t>(std::min<int64_t>(cost, INT32_MAX));
+          s.units[fam].push_back(u);
+        }
+      }
+    }
+  }
+
+  // longest-processing-time first: the dispatcher hands out workgroups in order, so the
+  // expensive units start early and the short ones fill the tail
+  for (int fam = 0; fam < FAM_COUNT; ++fam) {
+    std::stable_sort(s.units[fam].begin(), s.units[fam].end(),
+                     [](const Unit& x, const Unit& y) { return x.cost > y.cost; });
+  }
+  return kOk;
+}
+
+}  // namespace xattn

@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
+
+Tolerances: bf16 inputs max |out error| <= 2e-2, fp32 inputs <= 1e-5; lse <= 1e-3.
+The seeded workloads at full size are compared on whole outputs where the oracle is
+quick (tiny, Whisper decode, ragged prefill) and on sampled requests and heads where
+it is not (block-causal spans, GQA decode); small cases cover every kernel family,
+mask, head grouping, page size, split and edge case.
+"""
+import numpy as np
+import pytest
+
+from oracle import ref
+from ragged_attention_serving_amd import synth
+from tests.gpu_util import compare, log, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(w, gpu, chunk=0):
+    log(f"[parity] {w.name} chunk={chunk}")
+    out, lse, plan = run_gpu(w, gpu, chunk)
+    log(f"  schedule {plan.info()}")
+    ro, rl = ref.run_workload(w)
+    compare(out, lse, ro, rl, w.dtype, label=w.name)
+
+
+# ------------------------------------------------------------------ seeded workloads
+
+def test_tiny_cross_f32(gpu):
+    _full(synth.tiny_cross(0), gpu)
+
+
+def test_whisper_decode(gpu):
+    _full(synth.whisper_decode(0), gpu)
+
+
+def test_ragged_prefill(gpu):
+    _full(synth.ragged_prefill(0), gpu)
+
+
+def test_block_causal_sampled(gpu):
+    w = synth.block_causal(0)
+    log(f"[parity] {w.name} (sampled spans x heads)")
+    out, lse, plan = run_gpu(w, gpu)
+    log(f"  schedule {plan.info()}")
+    lens = w.qo_lens()
+    spans = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 5, 37})
+    heads = [0, 7, 15]
+    ro, rl = ref.run_workload(w, requests=spans, heads=heads)
+    rows = np.concatenate([np.arange(w.qo_indptr[s], w.qo_indptr[s + 1]) for s in spans])
+    compare(out[rows][:, heads], lse[rows][:, heads], ro[rows][:, heads], rl[rows][:, heads],
+            w.dtype, label=f"{w.name} spans {spans} heads {heads}")
+    assert np.isfinite(lse).all() and not np.isnan(out).any()
+
+
+def test_gqa_decode_sampled(gpu):
+    w = synth.gqa_decode(0)
+    log(f"[parity] {w.name} (sampled requests)")
+    out, lse, plan = run_gpu(w, gpu)
+    log(f"  schedule {plan.info()}")
+    kv = w.kv_lens()
+    reqs = sorted({int(np.argmax(kv)), int(np.argmin(kv)), 0, 100, 255})
+    ro, rl = ref.run_workload(w, requests=reqs)
+    compare(out[reqs], lse[reqs], ro[reqs], rl[reqs], w.dtype, label=f"{w.name} requests {reqs}")
+    assert np.isfinite(lse).all() and not np.isnan(out).any()
+
+
+# ------------------------------------------------------------------ small cases
+
+SMALL = [
+    # (name, qo_lens, kv_lens, hq, hkv, d, page_size, mask, block, dtype)
+    ("decode_mha_d64", [1] * 9, [1, 2, 15, 16, 17, 100, 513, 1000, 64], 4, 4, 64, 16, 0, 0, "bf16"),
+    ("decode_gqa4_causal_d128", [1] * 6, [1, 7, 64, 65, 300, 2049], 8, 2, 128, 16, 1, 0, "bf16"),
+    ("decode_gqa8_d128", [1] * 3, [33, 500, 129], 16, 2, 128, 8, 0, 0, "bf16"),
+    ("decode_rows2_causal", [2, 1, 2], [5, 40, 300], 2, 2, 64, 4, 1, 0, "bf16"),
+    ("decode_rows8_mixed", [2, 4, 1], [9, 70, 33], 4, 2, 64, 3, 1, 0, "bf16"),
+    ("decode_block", [3, 1], [50, 130], 2, 1, 64, 16, 2, 16, "bf16"),
+    ("mma_none_d64", [9, 33, 128, 129, 300], [1500, 77, 300, 129, 1000], 2, 2, 64, 16, 0, 0, "bf16"),
+    ("mma_causal_d128", [40, 200, 129], [40, 260, 500], 2, 2, 128, 16, 1, 0, "bf16"),
+    ("mma_gqa_causal_d64", [20, 70], [50, 300], 8, 2, 64, 16, 1, 0, "bf16"),
+    ("mma_block_d128", [300, 65, 1], [300, 65, 1], 2, 2, 128, 1, 2, 64, "bf16"),
+    ("mma_block_odd", [100, 250], [130, 250], 2, 1, 64, 5, 2, 7, "bf16"),
+    ("mma_page3", [50, 10], [77, 30], 2, 2, 64, 3, 0, 0, "bf16"),
+    ("f32_all_masks_none", [1, 5, 2], [16, 40, 7], 2, 2, 16, 4, 0, 0, "f32"),
+    ("f32_causal_gqa", [3, 1, 6], [7, 13, 6], 4, 1, 32, 3, 1, 0, "f32"),
+    ("f32_block_d64", [10, 17], [10, 17], 2, 2, 64, 1, 2, 4, "f32"),
+    ("f32_long_d128", [2, 1], [3000, 1100], 2, 2, 128, 16, 0, 0, "f32"),
+    ("empty_requests", [0, 3, 0, 1], [5, 0, 9, 0], 2, 2, 64, 4, 0, 0, "bf16"),
+    ("empty_requests_mma", [0, 20, 0], [5, 0, 9], 2, 2, 64, 4, 0, 0, "bf16"),
+]
+
+
+def _small(case, seed=0, tail="normal"):
+    name, qo, kv, hq, hkv, d, ps, mask, blk, dt = case
+    return synth.paged_case(qo, kv, hq, hkv, d, ps, dtype=dt, mask_mode=mask, block_size=blk,
+                            seed=seed, name=name, tail=tail, extra_pages=3)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("chunk", [0, 64, 17])
+def test_small(case, chunk, gpu):
+    w = _small(case)
+    _full(w, gpu, chunk)
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[0] in
+                                  ("decode_mha_d64", "mma_none_d64", "mma_block_odd", "f32_causal_gqa",
+                                   "decode_gqa4_causal_d128")], ids=lambda c: c[0])
+def test_nan_poisoned_tails(case, gpu):
+    """Unused page slots and unreferenced pages hold NaN: none may reach a result."""
+    w = _small(case, seed=3, tail="nan")
+    _full(w, gpu, 0)
+    _full(w, gpu, 33)
+
+
+def test_single_key_chunks(gpu):
+    """Every key its own chunk: the merge sees up to hundreds of partials per row."""
+    w = synth.paged_case([1, 3, 40], [200, 3, 120], 4, 2, 64, 16, mask_mode=1, seed=4, name="chunk1")
+    _full(w, gpu, 1)
+
+
+def test_empty_batch(gpu):
+    import ragged_attention_serving_amd as xa
+    import torch
+    plan = xa.Plan().plan([0], [0], None, None, 2, 2, 64, 16, 1)
+    q = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=gpu)
+    k = torch.zeros((1, 16, 2, 64), dtype=torch.bfloat16, device=gpu)
+    out, lse = plan.run(q, k, k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 64)
+
+
+def test_without_lse(gpu):
+    w = _small(SMALL[6])
+    out, lse, _ = run_gpu(w, gpu, want_lse=False)
+    assert lse is None
+    ro, _ = ref.run_workload(w)
+    assert np.max(np.abs(out - ro)) <= 2e-2
+
+
+# ------------------------------------------------------------------ invariants and contracts
+
+def test_page_permutation_is_bitwise_invariant(gpu):
+    w = synth.paged_case([1, 1, 30, 200], [900, 40, 300, 700], 4, 2, 128, 16, mask_mode=1, seed=5)
+    out1, lse1, _ = run_gpu(w, gpu)
+    perm = np.random.default_rng(9).permutation(w.num_pages)
+    kp = np.empty_like(w.k_pages)
+    vp = np.empty_like(w.v_pages)
+    kp[perm] = w.k_pages
+    vp[perm] = w.v_pages
+    w.k_pages, w.v_pages = kp, vp
+    w.kv_page_indices = perm[w.kv_page_indices].astype(np.int32)
+    out2, lse2, _ = run_gpu(w, gpu)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_cache_is_never_written(gpu):
+    import torch
+    w = synth.paged_case([1, 50, 3], [300, 400, 30], 4, 4, 64, 16, seed=6)
+    q, k, v = (to_device(w.q, "bf16", gpu), to_device(w.k_pages, "bf16", gpu), to_device(w.v_pages, "bf16", gpu))
+    k0, v0 = k.clone(), v.clone()
+    for chunk in (0, 64):
+        run_gpu(w, gpu, chunk, tensors=(q, k, v))
+    torch.cuda.synchronize()
+    assert torch.equal(k.view(torch.int16), k0.view(torch.int16))
+    assert torch.equal(v.view(torch.int16), v0.view(torch.int16))
+
+
+def test_uniform_scores_closed_form(gpu):
+    """Q = 0: O is the mean of the visible values and lse = ln(visible count)."""
+    for mask, blk, qo, kv in ((0, 0, [1, 3, 100], [16, 40, 1500]), (1, 0, [1, 5, 150], [700, 9, 150]),
+                              (2, 64, [300, 64], [300, 64])):
+        w = synth.paged_case(qo, kv, 2, 2, 64, 16 if mask != 2 else 1, mask_mode=mask, block_size=blk, seed=7)
+        w.q = np.zeros_like(w.q)
+        out, lse, _ = run_gpu(w, gpu)
+        ro, rl = ref.run_workload(w)
+        compare(out, lse, ro, rl, "bf16", label=f"Q=0 mask {mask}")
+        for r in range(len(qo)):
+            for i in range(qo[r]):
+                pos = kv[r] - qo[r] + i
+                n = kv[r] if mask == 0 else (pos + 1 if mask == 1 else min((pos // blk + 1) * blk, kv[r]))
+                assert abs(lse[w.qo_indptr[r] + i, 0] - np.log(n)) < 1e-3
+
+
+def test_one_plan_many_layers(gpu):
+    """One plan serves several runs with different q/k/v (one per layer)."""
+    base = synth.paged_case([1, 40, 2], [500, 300, 60], 4, 2, 64, 16, mask_mode=1, seed=8)
+    plan = None
+    for layer in range(3):
+        w = synth.paged_case([1, 40, 2], [500, 300, 60], 4, 2, 64, 16, mask_mode=1, seed=100 + layer)
+        w.kv_page_indices = base.kv_page_indices
+        out, lse, plan = run_gpu(w, gpu, plan=plan) if plan is None else _run_existing(w, gpu, plan)
+        ro, rl = ref.run_workload(w)
+        compare(out, lse, ro, rl, "bf16", label=f"layer {layer}")
+
+
+def _run_existing(w, gpu, plan):
+    import torch
+    from tests.gpu_util import from_device
+    q, k, v = (to_device(w.q, w.dtype, gpu), to_device(w.k_pages, w.dtype, gpu), to_device(w.v_pages, w.dtype, gpu))
+    out, lse = plan.run(q, k, v)
+    torch.cuda.synchronize()
+    return from_device(out), lse.cpu().numpy().astype(np.float64), plan
+
+
+def test_double_buffered_plans_while_the_gpu_is_busy(gpu):
+    """Plan A, run A, plan B, run B while the stream is still busy with earlier work: the
+    second plan must not overwrite the staging that run A reads; a third plan waits for
+    the slot's fence. The stream is held by ordinary queued matrix products."""
+    import torch
+    wa = synth.paged_case([1, 30], [700, 300], 4, 2, 64, 16, mask_mode=1, seed=10)
+    wb = synth.paged_case([5, 1, 2], [20, 900, 64], 4, 2, 64, 16, mask_mode=1, seed=11)
+    ta = [to_device(x, "bf16", gpu) for x in (wa.q, wa.k_pages, wa.v_pages)]
+    tb = [to_device(x, "bf16", gpu) for x in (wb.q, wb.k_pages, wb.v_pages)]
+    x = torch.randn(4096, 4096, device=gpu)
+    torch.cuda.synchronize()
+    import ragged_attention_serving_amd as xa
+    plan = xa.Plan()
+    for _ in range(150):  # hundreds of milliseconds of queued work
+        x = torch.tanh(x @ x) * 0.01
+    plan.plan(wa.qo_indptr, wa.kv_indptr, wa.kv_page_indices, wa.kv_last_page_len, 4, 2, 64, 16,
+              wa.num_pages, 1)
+    oa, la = plan.run(*ta)
+    plan.plan(wb.qo_indptr, wb.kv_indptr, wb.kv_page_indices, wb.kv_last_page_len, 4, 2, 64, 16,
+              wb.num_pages, 1)
+    ob, lb = plan.run(*tb)
+    busy = not plan.ready()
+    # a third plan reuses slot A: it waits on the fence of run A
+    plan.plan(wa.qo_indptr, wa.kv_indptr, wa.kv_page_indices, wa.kv_last_page_len, 4, 2, 64, 16,
+              wa.num_pages, 1)
+    oc, lc = plan.run(*ta)
+    torch.cuda.synchronize()
+    log(f"  next slot busy while queued: {busy}")
+    from tests.gpu_util import from_device
+    ra, rla = ref.run_workload(wa)
+    rb, rlb = ref.run_workload(wb)
+    compare(from_device(oa), la.cpu().numpy().astype(np.float64), ra, rla, "bf16", label="plan A")
+    compare(from_device(ob), lb.cpu().numpy().astype(np.float64), rb, rlb, "bf16", label="plan B")
+    compare(from_device(oc), lc.cpu().numpy().astype(np.float64), ra, rla, "bf16", label="plan A again")
+    assert busy

@@ -37,6 +37,63 @@ static int fail(std::string& err, int code, const std::string& msg) {
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+
+// Workgroup i of a launch runs on XCD i % kXcds (round-robin dispatch). Groups of units
+// that share a (request, KV head) are assigned whole to one XCD (greedy, largest group
+// first, to the least loaded XCD that still has room), each group's units back to back
+// in that XCD's sequence, largest first; position p of the launch then takes the next
+// unit of XCD p % kXcds.
+static void order_for_xcds(std::vector<Unit>& units) {
+  const int64_t n = static_cast<int64_t>(units.size());
+  if (n <= kXcds) {
+    std::stable_sort(units.begin(), units.end(), [](const Unit& x, const Unit& y) { return x.cost > y.cost; });
+    return;
+  }
+  std::stable_sort(units.begin(), units.end(), [](const Unit& x, const Unit& y) {
+    if (x.r != y.r) return x.r < y.r;
+    if (x.hk != y.hk) return x.hk < y.hk;
+    return x.cost > y.cost;
+  });
+  struct Group {
+    int64_t begin, end, cost;
+  };
+  std::vector<Group> groups;
+  for (int64_t i = 0; i < n;) {
+    int64_t j = i, c = 0;
+    while (j < n && units[j].r == units[i].r && units[j].hk == units[i].hk) c += units[j++].cost;
+    groups.push_back(Group{i, j, c});
+    i = j;
+  }
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.cost > b.cost; });
+  int64_t cap[kXcds], load[kXcds];
+  std::vector<Unit> queue[kXcds];
+  for (int x = 0; x < kXcds; ++x) {
+    cap[x] = (n - x + kXcds - 1) / kXcds;
+    load[x] = 0;
+  }
+  for (const Group& gr : groups) {
+    int64_t left = gr.end - gr.begin, at = gr.begin;
+    while (left > 0) {
+      int best = -1;
+      for (int x = 0; x < kXcds; ++x)
+        if (cap[x] >= left && (best < 0 || load[x] < load[best])) best = x;
+      if (best < 0)  // no XCD has room for the rest of the group: use the emptiest
+        for (int x = 0; x < kXcds; ++x)
+          if (cap[x] > 0 && (best < 0 || cap[x] > cap[best])) best = x;
+      const int64_t take = std::min(left, cap[best]);
+      for (int64_t k = 0; k < take; ++k) {
+        load[best] += units[at].cost;
+        queue[best].push_back(units[at++]);
+      }
+      cap[best] -= take;
+      left -= take;
+    }
+  }
+  std::vector<Unit> out(n);
+  for (int64_t p = 0; p < n; ++p) out[p] = queue[p % kXcds][p / kXcds];
+  units.swap(out);
+}
+
 int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
   s = Schedule();
   const int B = a.batch;
@@ -108,9 +165,24 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
   }
 
   // ---- classify requests and size the work per family
+  // Requests with few query rows (tokens x grouped heads) go to the decode kernel, the
+  // rest to the MFMA tile kernel. In a batch whose KV traffic is mostly prefill, the few
+  // short requests ride along in the tile launch instead (one launch, no second kernel).
+  bool small_to_tiles = false;
+  if (a.dtype != 0) {
+    int64_t short_kv = 0, tile_kv = 0;
+    for (int r = 0; r < B; ++r) {
+      const int64_t qo = s.reqs[4 * r + 1], kv = s.reqs[4 * r + 2];
+      if (qo == 0) continue;
+      const int64_t rows = qo * g;
+      if (rows <= kDecMaxRows) short_kv += kv;
+      else tile_kv += kv * ((rows + kMmaRows - 1) / kMmaRows);
+    }
+    small_to_tiles = tile_kv > 0 && short_kv <= tile_kv;
+  }
   auto family_of = [&](int64_t rows) -> int {
     if (a.dtype == 0) return FAM_F32;
-    return rows <= kDecMaxRows ? FAM_DEC : FAM_MMA;
+    return rows <= kDecMaxRows && !small_to_tiles ? FAM_DEC : FAM_MMA;
   };
   auto rows_per_unit = [&](int fam) -> int64_t {
     return fam == FAM_F32 ? kF32Rows : fam == FAM_DEC ? kDecMaxRows : kMmaRows;
@@ -124,6 +196,7 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
 
   int64_t fam_work[FAM_COUNT] = {0, 0, 0};   // key-heads (decode) or tile count (mma)
   int64_t fam_maxkv[FAM_COUNT] = {0, 0, 0};
+  int64_t fam_units[FAM_COUNT] = {0, 0, 0};  // units before any split
   int dec_rows = 0;
   for (int r = 0; r < B; ++r) {
     const int64_t qo = s.reqs[4 * r + 1];
@@ -137,6 +210,7 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
       const int64_t hi = tile_hi(r, row_end);
       fam_work[fam] += (fam == FAM_MMA ? 1 : hi) * a.hkv;
       fam_maxkv[fam] = std::max(fam_maxkv[fam], hi);
+      fam_units[fam] += a.hkv;
     }
     // visible pairs: exact count per query row, for the metric
     const int64_t kv = s.reqs[4 * r + 2];
@@ -159,8 +233,17 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
     } else if (fam == FAM_F32) {
       c = kF32MaxChunk;
     } else if (fam == FAM_DEC) {
-      // about 2048 units of at least 256 keys: several waves of work per compute unit
-      c = std::max<int64_t>(256, round_up(ceil_div(std::max<int64_t>(fam_work[fam], 1), 2048), 64));
+      // The decode kernel keeps up to 8 workgroups resident per compute unit (2048 on the
+      // chip). If the unsplit units fill the chip in one round and are about the same
+      // length, they all start at once and finish together: no split, no merge.
+      // Otherwise aim for about 2048 units (longer units run more efficiently, so the
+      // chunk is not made any shorter than that needs).
+      const int64_t mean = ceil_div(std::max<int64_t>(fam_work[fam], 1), std::max<int64_t>(fam_units[fam], 1));
+      if (fam_units[fam] >= 1024 && fam_units[fam] <= 2048 && fam_maxkv[fam] * 4 <= mean * 5) {
+        c = std::max<int64_t>(fam_maxkv[fam], 1);
+      } else {
+        c = std::max<int64_t>(256, round_up(ceil_div(std::max<int64_t>(fam_work[fam], 1), 2048), 64));
+      }
     } else {
       // split only when there are too few query tiles to fill 256 compute units twice
       const int64_t tiles = std::max<int64_t>(fam_work[fam], 1);
@@ -172,6 +255,8 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
       }
     }
     if (fam == FAM_F32) c = std::min<int64_t>(c, kF32MaxChunk);
+    // a paged MFMA unit stages its page indices in LDS: keep its span within kMmaMaxPages
+    if (fam == FAM_MMA && !s.identity) c = std::min<int64_t>(c, static_cast<int64_t>(kMmaMaxPages - 2) * a.page_size);
     c = std::min<int64_t>(std::max<int64_t>(c, 1), INT32_MAX);
     chunk[fam] = c;
     s.chunk[fam] = static_cast<int32_t>(c);
@@ -194,8 +279,9 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
         // equal chunks, rounded to whole 64-key tiles when that keeps the count; a forced
         // chunk length is taken as given
         int64_t step = hi <= 0 ? 1 : ceil_div(hi, nch);
-        if (a.force_chunk > 0) step = chunk[fam];
-        else if (nch > 1 && ceil_div(hi, round_up(step, 64)) == nch) step = round_up(step, 64);
+        if (a.force_chunk > 0) step = chunk[fam];  // the forced length, after the caps above
+        else if (nch > 1 && round_up(step, 64) <= chunk[fam] && ceil_div(hi, round_up(step, 64)) == nch)
+          step = round_up(step, 64);
         int32_t base = -1;
         if (nch > 1) {
           if (s.ws_rows + nch * nrows > INT32_MAX) return fail(err, kErrInvalid, "workspace too large");
@@ -229,12 +315,14 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
     }
   }
 
-  // longest-processing-time first: the dispatcher hands out workgroups in order, so the
-  // expensive units start early and the short ones fill the tail
-  for (int fam = 0; fam < FAM_COUNT; ++fam) {
-    std::stable_sort(s.units[fam].begin(), s.units[fam].end(),
-                     [](const Unit& x, const Unit& y) { return x.cost > y.cost; });
-  }
+  // Decode units read disjoint KV: longest-processing-time first (the dispatcher hands
+  // out workgroups in order, so the expensive units start early and the short ones fill
+  // the tail). Tile units of one (request, KV head) re-read the same keys: keep each such
+  // group on one XCD, back to back, so the re-reads hit that XCD's L2.
+  std::stable_sort(s.units[FAM_DEC].begin(), s.units[FAM_DEC].end(),
+                   [](const Unit& x, const Unit& y) { return x.cost > y.cost; });
+  order_for_xcds(s.units[FAM_MMA]);
+  order_for_xcds(s.units[FAM_F32]);
   return kOk;
 }
 

@@ -16,6 +16,10 @@ constexpr int kF32Rows = 4;    // fp32 kernel: scores of a chunk kept in LDS per
 constexpr int kDecMaxRows = 8; // decode kernel: rows held in registers per lane
 constexpr int kMmaRows = 128;  // MFMA kernel: 4 waves x 32 query columns
 constexpr int kF32MaxChunk = 1024;
+// MFMA kernel: page indices of one unit staged in LDS; a unit may span at most this many pages
+constexpr int kMmaMaxPages = 1024;
+// XCDs of an MI355X: workgroup i of a launch is dispatched to XCD i % kXcds
+constexpr int kXcds = 8;
 
 struct PlanArgs {
   const int32_t* qo_indptr = nullptr;

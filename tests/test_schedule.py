@@ -40,8 +40,12 @@ def check_schedule(qo_lens, kv_lens, hq, hkv, page_size, mask, block, dtype, for
         assert 0 <= r < B and 0 <= hk < hkv and qo_lens[r] > 0
         assert 1 <= nrows <= caps[f] and 0 <= row0 and row0 + nrows <= rows
         assert 0 <= kv0 <= kv1 <= kv_lens[r]
-        want_f = 0 if dtype == "f32" else (1 if rows <= 8 else 2)
-        assert f == want_f
+        if dtype == "f32":
+            assert f == 0
+        elif rows > 8:
+            assert f == 2
+        else:
+            assert f in (1, 2)
         if force_chunk:
             assert kv1 - kv0 <= force_chunk
         for rr in range(nrows):
@@ -77,10 +81,27 @@ def check_schedule(qo_lens, kv_lens, hq, hkv, page_size, mask, block, dtype, for
                 out_written[out_row] = out_written.get(out_row, 0) + 1
     assert all(v == 1 for v in out_written.values())
     assert len(merges) == info["num_merge_rows"]
-    # longest first within each family
-    for f in range(3):
-        c = units[fam == f][:, 7]
-        assert np.all(np.diff(c) <= 0)
+    # decode units: longest first
+    c = units[fam == 1][:, 7]
+    assert np.all(np.diff(c) <= 0)
+    # tile units: each (request, kv head) group on one XCD (launch position mod 8), its units
+    # consecutive in that XCD's sequence (a group is split only when no XCD has room left)
+    for f in (0, 2):
+        fu = units[fam == f]
+        if len(fu) <= 8:
+            continue
+        split = 0
+        groups = {}
+        for pos, u in enumerate(fu):
+            groups.setdefault((int(u[0]), int(u[1])), []).append(pos)
+        for key, pos in groups.items():
+            res = {p % 8 for p in pos}
+            if len(res) > 1:
+                split += 1
+                continue
+            seq = [p // 8 for p in pos]
+            assert seq == list(range(seq[0], seq[0] + len(seq))), key
+        assert split <= max(8, len(groups) // 4), (split, len(groups))
     return info, units, merges
 
 
@@ -142,3 +163,28 @@ def test_visible_pairs_counts_the_mask():
     info, _, _ = check_schedule([64], [64], 1, 1, 1, 2, 16, "bf16")
     # block-causal, 4 blocks of 16: row i sees (i // 16 + 1) * 16 keys
     assert info["visible_pairs"] == sum((i // 16 + 1) * 16 for i in range(64))
+
+
+@pytest.mark.parametrize("ps,chunk", [(1, 0), (1, 5000), (16, 0), (3, 0), (16, 100000)])
+def test_mma_units_stay_within_the_page_cap(ps, chunk):
+    """A paged MFMA unit stages its page indices in LDS: it may span at most 1024 pages."""
+    kv = [40000, 17000, 2048] if ps > 1 else [9000, 2500, 300]
+    qo = [300, 9, 129]
+    kv_indptr, idx, last, total = synth.page_table(kv, ps, None)
+    info, units, _ = xa.xattn_schedule(synth.indptr(qo), kv_indptr, idx, last, 4, 4, 64, ps, total, 0, 0,
+                                       "bf16", chunk)
+    mma = units[sum(info["num_units"][:2]):]
+    assert len(mma)
+    for u in mma:
+        kv0, kv1 = int(u[4]), int(u[5])
+        if kv1 > kv0:
+            assert (kv1 - 1) // ps - kv0 // ps + 1 <= 1024, (kv0, kv1)
+    check_schedule(qo, kv, 4, 4, ps, 0, 0, "bf16", force_chunk=chunk)
+
+
+def test_short_requests_ride_with_prefill():
+    """A batch whose KV traffic is mostly prefill runs its short requests in the tile launch."""
+    info, units, _ = check_schedule([300, 1, 2, 200], [1500] * 4, 4, 4, 16, 0, 0, "bf16")
+    assert info["num_units"][1] == 0 and info["num_units"][2] > 0
+    info, units, _ = check_schedule([1] * 30 + [20], [1500] * 31, 4, 4, 16, 0, 0, "bf16")
+    assert info["num_units"][1] > 0 and info["num_units"][2] > 0

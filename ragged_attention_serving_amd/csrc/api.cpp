@@ -14,7 +14,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/xattn.h"
+#include "xattn.h"
 #include "kernels.h"
 #include "partition.h"
 
@@ -183,10 +183,11 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
   Schedule s;
   std::string err;
-  const xattn::PlanArgs a =
+  xattn::PlanArgs a =
       make_args(qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, batch_size, num_qo_heads,
                 num_kv_heads, head_dim, page_size, num_pages, mask_mode, block_size, sm_scale, dtype,
                 env_int("XATTN_FORCE_CHUNK", 0));
+  a.tile_rows = env_int("XATTN_TILE_ROWS", 0);
   const int rc = xattn::build_schedule(a, s, err);
   if (rc != XATTN_OK) return set_err(rc, err);
   if (env_int("XATTN_LOG", 0)) log_schedule(s);
@@ -328,6 +329,7 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   }
   p.mask = sl.mask;
   p.block = sl.mask == 2 ? sl.block : 1;
+  p.tile_rows = s.tile_rows;
   p.scale = s.scale;
   p.scale_log2 = s.scale * 1.4426950408889634f;
 

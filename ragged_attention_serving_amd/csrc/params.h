@@ -25,6 +25,7 @@ struct AttnParams {
   int32_t page_size;
   int32_t page_shift;   // log2(page_size) when a power of two, else -1
   int32_t mask, block;
+  int32_t tile_rows;    // query rows per MFMA tile unit (128 or 256)
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
 };

@@ -111,6 +111,9 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
   if (a.dtype == 1 && a.d != 64 && a.d != 128)
     return fail(err, kErrUnsupported, "bf16 head_dim must be 64 or 128");
   if (a.force_chunk < 0) return fail(err, kErrInvalid, "force_chunk < 0");
+  if (a.tile_rows != 0 && a.tile_rows != 128 && a.tile_rows != 256)
+    return fail(err, kErrInvalid, "tile_rows must be 128 or 256");
+  s.tile_rows = a.tile_rows ? a.tile_rows : kMmaRows;
 
   const int g = a.hq / a.hkv;
   s.group = g;
@@ -176,7 +179,7 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
       if (qo == 0) continue;
       const int64_t rows = qo * g;
       if (rows <= kDecMaxRows) short_kv += kv;
-      else tile_kv += kv * ((rows + kMmaRows - 1) / kMmaRows);
+      else tile_kv += kv * ((rows + s.tile_rows - 1) / s.tile_rows);
     }
     small_to_tiles = tile_kv > 0 && short_kv <= tile_kv;
   }
@@ -185,7 +188,7 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
     return rows <= kDecMaxRows && !small_to_tiles ? FAM_DEC : FAM_MMA;
   };
   auto rows_per_unit = [&](int fam) -> int64_t {
-    return fam == FAM_F32 ? kF32Rows : fam == FAM_DEC ? kDecMaxRows : kMmaRows;
+    return fam == FAM_F32 ? kF32Rows : fam == FAM_DEC ? kDecMaxRows : s.tile_rows;
   };
   // KV range [0, hi) a row tile needs: up to the last key its last row sees.
   auto tile_hi = [&](int r, int64_t row_end) -> int64_t {

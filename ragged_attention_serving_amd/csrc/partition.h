@@ -14,7 +14,7 @@ enum Family { FAM_F32 = 0, FAM_DEC = 1, FAM_MMA = 2, FAM_COUNT = 3 };
 // Rows (query tokens x grouped heads) per unit for each family.
 constexpr int kF32Rows = 4;    // fp32 kernel: scores of a chunk kept in LDS per row
 constexpr int kDecMaxRows = 8; // decode kernel: rows held in registers per lane
-constexpr int kMmaRows = 128;  // MFMA kernel: 4 waves x 32 query columns
+constexpr int kMmaRows = 128;  // MFMA kernel, default: 4 waves x 32 query columns
 constexpr int kF32MaxChunk = 1024;
 // MFMA kernel: page indices of one unit staged in LDS; a unit may span at most this many pages
 constexpr int kMmaMaxPages = 1024;
@@ -32,6 +32,7 @@ struct PlanArgs {
   float sm_scale = 0.f;
   int32_t dtype = 0;
   int32_t force_chunk = 0;  // > 0: split every context into chunks of this many keys
+  int32_t tile_rows = 0;    // MFMA tile height, 128 or 256 (0: kMmaRows)
 };
 
 // One unit of work: a request's kv head, a range of its query rows, a KV range.
@@ -51,6 +52,7 @@ struct Schedule {
   std::vector<int32_t> pages;  // copy of kv_page_indices (empty: identity table)
   int64_t ws_rows = 0;
   int32_t dec_rows = 0;
+  int32_t tile_rows = kMmaRows;
   int32_t chunk[FAM_COUNT] = {0, 0, 0};
   int64_t total_kv = 0;
   int64_t visible_pairs = 0;

@@ -238,3 +238,15 @@ def test_double_buffered_plans_while_the_gpu_is_busy(gpu):
     compare(from_device(ob), lb.cpu().numpy().astype(np.float64), rb, rlb, "bf16", label="plan B")
     compare(from_device(oc), lc.cpu().numpy().astype(np.float64), ra, rla, "bf16", label="plan A again")
     assert busy
+
+
+@pytest.mark.parametrize("rows", [128, 256])
+def test_tile_kernel_variants(rows, gpu, monkeypatch):
+    """Both MFMA tile heights, on tiles with tails, masks and splits."""
+    monkeypatch.setenv("XATTN_TILE_ROWS", str(rows))
+    for case in ("mma_none_d64", "mma_causal_d128", "mma_block_odd", "mma_gqa_causal_d64"):
+        w = _small([c for c in SMALL if c[0] == case][0])
+        _full(w, gpu, 0)
+        _full(w, gpu, 130)
+    w = synth.ragged_case([700, 65, 300], 2, 128, block_size=64, seed=12, name="block_causal_small")
+    _full(w, gpu, 0)

@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "fp32": "ragged_attention_serving_amd/csrc/attn_f32.hip",
     "merge": "ragged_attention_serving_amd/csrc/merge.hip",
 }
+TIMING_EVERY = 5  # kernel events on every 5th timed run (a pair of events costs several us)
 KERNEL_NAMES = {"decode": "attn_decode_kernel", "mfma": "attn_mma_kernel", "fp32": "attn_f32_kernel",
                 "merge": "merge_kernel"}
 
@@ -91,8 +92,9 @@ def measure(w, steps, warmup, dev, cold_steps=5):
         plan.run(q, k, v, out, lse)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` runs, synchronised on both sides
-    plan.set_timing(True)
+    # timed region: exactly `steps` runs, synchronised on both sides; HIP events around the
+    # kernels of every TIMING_EVERY-th run give the per-kernel durations
+    plan.set_timing(TIMING_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -100,7 +102,7 @@ def measure(w, steps, warmup, dev, cold_steps=5):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     stages = plan.timing()
-    plan.set_timing(False)
+    plan.set_timing(0)
 
     # cold runs: 1 GiB written between runs to evict L2 and the Infinity Cache
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)

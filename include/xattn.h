@@ -89,8 +89,11 @@ enum xattn_status {
  * plan            in/out. *plan == NULL creates a handle; otherwise the new schedule
  *                 is written into the handle's other slot (two slots: pinned host
  *                 staging + device copy + fp32 split workspace each). Before a slot is
- *                 rewritten the call waits on that slot's fence, which covers its
- *                 host-to-device copy and every run that read it.
+ *                 rewritten the call waits until the slot's previous host-to-device
+ *                 copy is done, and until every run that read the slot is done or is
+ *                 ordered before the new copy by the stream (runs on the plan's stream
+ *                 are; runs on other streams are waited for, and a plan on another
+ *                 stream than the slot last used waits for that stream).
  * qo_indptr       [batch_size + 1]; qo_indptr[0] == 0, non-decreasing.
  * kv_indptr       [batch_size + 1]; page counts; kv_indptr[0] == 0, non-decreasing.
  * kv_page_indices [kv_indptr[batch_size]], each in [0, num_pages); NULL means the
@@ -132,15 +135,18 @@ XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int
  * stream               hipStream_t (NULL: the null stream).
  *
  * Returns XATTN_ERR_INVALID_ARG for a handle with no schedule, a NULL pointer that
- * the schedule needs or a misaligned pointer, XATTN_ERR_HIP for a launch failure. Device faults
- * surface at the caller's next synchronisation. Pointers are borrowed until the
- * stream passes the run.
+ * the schedule needs or a misaligned pointer, XATTN_ERR_HIP for a launch failure.
+ * Device faults surface at the caller's next synchronisation. Pointers are borrowed
+ * until the stream passes the run. A run on another stream than the plan's waits for
+ * the schedule's copy and records an event that the next plan into this slot waits
+ * for; a run on the plan's stream records nothing. Streams used by runs must stay
+ * valid until the handle's next-but-one xattn_plan or its destruction.
  */
 XATTN_API int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
               void* out, float* lse, void* stream);
 
-/* 1 if the next xattn_plan on this handle would not wait on a fence, 0 if it would,
- * negative on error. Never blocks. */
+/* 1 if the next xattn_plan on this handle (on the same stream) would not wait, 0 if it
+ * would, negative on error. Never blocks. */
 XATTN_API int xattn_plan_ready(xattn_plan_t plan);
 
 /* Waits on both slot fences, then frees the handle. NULL is ignored. */
@@ -181,14 +187,15 @@ XATTN_API int xattn_schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
 XATTN_API int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info);
 
 /*
- * Kernel timing. With enable != 0, every later xattn_run on this handle records a pair
- * of HIP events around each kernel it launches, on the run's stream (at most 65536
- * pairs are kept; later runs are not recorded until the next collection).
+ * Kernel timing. With every > 0, every `every`-th later xattn_run on this handle
+ * records a pair of HIP events around each kernel it launches, on the run's stream (at
+ * most 65536 pairs are kept; later runs are not recorded until the next collection).
+ * Sampling keeps the cost of the events (a few microseconds per pair) off most runs.
  * xattn_plan_timing waits for the recorded events, writes the summed milliseconds
  * and the launch count per stage {0 fp32, 1 bf16 decode, 2 bf16 MFMA tile, 3 merge}
- * into ms[4] and launches[4], and clears the records. enable == 0 stops recording.
+ * into ms[4] and launches[4], and clears the records. every <= 0 stops recording.
  */
-XATTN_API int xattn_plan_set_timing(xattn_plan_t plan, int enable);
+XATTN_API int xattn_plan_set_timing(xattn_plan_t plan, int every);
 XATTN_API int xattn_plan_timing(xattn_plan_t plan, double* ms, int32_t* launches);
 
 #ifdef __cplusplus

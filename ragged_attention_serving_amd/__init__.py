@@ -199,8 +199,9 @@ def xattn_plan_info(handle) -> dict:
     return info.as_dict()
 
 
-def xattn_plan_set_timing(handle, enable: bool) -> None:
-    _check(lib().xattn_plan_set_timing(handle, 1 if enable else 0))
+def xattn_plan_set_timing(handle, every: int) -> None:
+    """Record kernel events on every `every`-th run (0 or False: off, True: every run)."""
+    _check(lib().xattn_plan_set_timing(handle, int(every)))
 
 
 def xattn_plan_timing(handle) -> dict:
@@ -270,8 +271,8 @@ class Plan:
     def info(self) -> dict:
         return xattn_plan_info(self._h)
 
-    def set_timing(self, enable: bool = True) -> None:
-        xattn_plan_set_timing(self._h, enable)
+    def set_timing(self, every: int = 1) -> None:
+        xattn_plan_set_timing(self._h, every)
 
     def timing(self) -> dict:
         return xattn_plan_timing(self._h)

@@ -4,8 +4,17 @@
 // FlashInferCrossManager.force_double_buffer: a plan is staged in a pinned host
 // buffer and copied to the device with a non-blocking copy, so planning step N+1
 // into the same buffer before step N's copy (and the runs that read it) retired would
-// race. Each handle therefore owns two slots; plan N writes slot N % 2 after waiting
-// on that slot's fence, and run reads the latest slot and re-arms its fence.
+// race. Each handle therefore owns two slots; plan N writes slot N % 2, and run reads
+// the latest slot.
+//
+// Before a slot is rewritten:
+//  * its previous host-to-device copy must have read the pinned buffer (the slot's
+//    `uploaded` event);
+//  * every run that read the slot's device copy or workspace must be done, or be
+//    ordered before the new copy. Runs on the plan's own stream are: the new copy is
+//    queued behind them. A run on another stream records the slot's fence, and a plan
+//    on another stream than the one the slot last used drains that stream first.
+// So the common case, plan and runs on one stream, records nothing per run.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -50,9 +59,13 @@ struct Slot {
   size_t dev_cap = 0;
   float* ws = nullptr;  // [ws_rows][d] partial O, then [ws_rows] partial lse
   size_t ws_cap = 0;    // bytes
-  hipEvent_t fence = nullptr;     // covers the slot's copy and every run that read it
+  hipEvent_t fence = nullptr;     // drains the slot's previous plan stream on a stream change
   hipEvent_t uploaded = nullptr;  // the slot's host-to-device copy
-  bool fenced = false;
+  void* plan_stream = nullptr;    // stream of that copy
+  bool uploaded_rec = false;      // `uploaded` was recorded
+  // runs on streams other than the plan's: one event per stream, after its latest run
+  std::vector<std::pair<void*, hipEvent_t>> foreign;
+  size_t foreign_live = 0;        // entries recorded since the slot was last planned
   bool ready = false;
   // schedule summary and device offsets (in int32 words from dev)
   Schedule sched;
@@ -71,7 +84,8 @@ struct xattn_plan_s {
   Slot slot[2];
   int cur = -1;
   int device = 0;
-  bool timing = false;
+  int timing_every = 0;  // record kernel events on every n-th run (0: off)
+  int64_t runs = 0;
   std::vector<hipEvent_t> event_pool;
   std::vector<TimingRec> timing_recs;
 };
@@ -219,10 +233,21 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
     if ((e = hipEventCreateWithFlags(&sl.uploaded, hipEventDisableTiming)) != hipSuccess)
       return fail(hip_err(e, "hipEventCreate"));
   }
-  if (sl.fenced) {
-    // the slot's previous copy and every run that read it must retire before reuse
-    if ((e = hipEventSynchronize(sl.fence)) != hipSuccess) return fail(hip_err(e, "hipEventSynchronize"));
+  if (sl.uploaded_rec) {
+    // the previous copy out of the pinned buffer must be done before it is rewritten
+    if ((e = hipEventSynchronize(sl.uploaded)) != hipSuccess) return fail(hip_err(e, "hipEventSynchronize"));
+    if (stream != sl.plan_stream) {
+      // runs on the slot's old stream are not ordered before a copy on this one: drain it
+      if ((e = hipEventRecord(sl.fence, static_cast<hipStream_t>(sl.plan_stream))) != hipSuccess)
+        return fail(hip_err(e, "hipEventRecord"));
+      if ((e = hipEventSynchronize(sl.fence)) != hipSuccess) return fail(hip_err(e, "hipEventSynchronize"));
+    }
   }
+  for (size_t i = 0; i < sl.foreign_live; ++i) {
+    // runs that used another stream than the plan's
+    if ((e = hipEventSynchronize(sl.foreign[i].second)) != hipSuccess) return fail(hip_err(e, "hipEventSynchronize"));
+  }
+  sl.foreign_live = 0;
 
   // device image: reqs | units per family | merges | page indices (int32 words)
   size_t words = 0;
@@ -263,8 +288,8 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   if ((e = hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, strm)) != hipSuccess)
     return fail(hip_err(e, "hipMemcpyAsync"));
   if ((e = hipEventRecord(sl.uploaded, strm)) != hipSuccess) return fail(hip_err(e, "hipEventRecord"));
-  if ((e = hipEventRecord(sl.fence, strm)) != hipSuccess) return fail(hip_err(e, "hipEventRecord"));
-  sl.fenced = true;
+  sl.uploaded_rec = true;
+  sl.plan_stream = stream;
 
   sl.off_reqs = off_reqs;
   for (int f = 0; f < xattn::FAM_COUNT; ++f) sl.off_units[f] = off_units[f];
@@ -301,7 +326,11 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if ((e = hipStreamWaitEvent(strm, sl.uploaded, 0)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+  // a run on another stream than the plan's waits for the schedule's copy; on the same
+  // stream the copy already precedes it
+  if (stream != sl.plan_stream) {
+    if ((e = hipStreamWaitEvent(strm, sl.uploaded, 0)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+  }
 
   const int32_t* dev = static_cast<const int32_t*>(sl.dev);
   AttnParams p{};
@@ -334,7 +363,8 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   p.scale_log2 = s.scale * 1.4426950408889634f;
 
   // optional per-kernel events (xattn_plan_set_timing)
-  const bool timed = plan->timing && plan->timing_recs.size() < kMaxTimingRecs;
+  const bool timed = plan->timing_every > 0 && plan->runs++ % plan->timing_every == 0 &&
+                     plan->timing_recs.size() < kMaxTimingRecs;
   auto event = [&](hipEvent_t* ev) -> hipError_t {
     if (!plan->event_pool.empty()) {
       *ev = plan->event_pool.back();
@@ -375,18 +405,38 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
     if ((e = xattn::launch_merge(p, sl.dtype, strm)) != hipSuccess) return hip_err(e, "merge kernel launch");
     if ((e = end()) != hipSuccess) return hip_err(e, "timing event");
   }
-  if ((e = hipEventRecord(sl.fence, strm)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  if (stream != sl.plan_stream) {
+    // not ordered before the slot's next copy by the stream: fence this stream
+    size_t i = 0;
+    while (i < sl.foreign_live && sl.foreign[i].first != stream) ++i;
+    if (i == sl.foreign_live) {
+      if (i == sl.foreign.size()) {
+        hipEvent_t ev = nullptr;
+        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_err(e, "hipEventCreate");
+        sl.foreign.emplace_back(stream, ev);
+      }
+      sl.foreign[i].first = stream;
+      ++sl.foreign_live;
+    }
+    if ((e = hipEventRecord(sl.foreign[i].second, strm)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  }
   return XATTN_OK;
 }
 
 int xattn_plan_ready(xattn_plan_t plan) {
   if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
   const Slot& sl = plan->slot[plan->cur < 0 ? 0 : (plan->cur ^ 1)];
-  if (!sl.fenced) return 1;
-  const hipError_t e = hipEventQuery(sl.fence);
-  if (e == hipSuccess) return 1;
-  if (e == hipErrorNotReady) return 0;
-  return hip_err(e, "hipEventQuery");
+  if (sl.uploaded_rec) {
+    const hipError_t e = hipEventQuery(sl.uploaded);
+    if (e == hipErrorNotReady) return 0;
+    if (e != hipSuccess) return hip_err(e, "hipEventQuery");
+  }
+  for (size_t i = 0; i < sl.foreign_live; ++i) {
+    const hipError_t e = hipEventQuery(sl.foreign[i].second);
+    if (e == hipErrorNotReady) return 0;
+    if (e != hipSuccess) return hip_err(e, "hipEventQuery");
+  }
+  return 1;
 }
 
 int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info) {
@@ -396,9 +446,10 @@ int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info) {
   return XATTN_OK;
 }
 
-int xattn_plan_set_timing(xattn_plan_t plan, int enable) {
+int xattn_plan_set_timing(xattn_plan_t plan, int every) {
   if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
-  plan->timing = enable != 0;
+  plan->timing_every = every > 0 ? every : 0;
+  plan->runs = 0;
   return XATTN_OK;
 }
 
@@ -432,7 +483,11 @@ void xattn_plan_destroy(xattn_plan_t plan) {
   }
   for (hipEvent_t ev : plan->event_pool) (void)hipEventDestroy(ev);
   for (Slot& sl : plan->slot) {
-    if (sl.fenced && sl.fence) (void)hipEventSynchronize(sl.fence);
+    // runs on the plan's stream and on other streams must be done before the buffers go
+    if (sl.uploaded_rec && sl.fence && hipEventRecord(sl.fence, static_cast<hipStream_t>(sl.plan_stream)) == hipSuccess)
+      (void)hipEventSynchronize(sl.fence);
+    for (size_t i = 0; i < sl.foreign_live; ++i) (void)hipEventSynchronize(sl.foreign[i].second);
+    for (auto& f : sl.foreign) (void)hipEventDestroy(f.second);
     if (sl.fence) (void)hipEventDestroy(sl.fence);
     if (sl.uploaded) (void)hipEventDestroy(sl.uploaded);
     if (sl.host) (void)hipHostFree(sl.host);

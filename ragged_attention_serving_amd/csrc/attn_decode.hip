@@ -9,26 +9,36 @@
 // summed over the 8 lanes with DPP. Each lane keeps an online softmax (running max,
 // sum and its slice of O in fp32) for the keys of its lane group; the 32 partial
 // states of the workgroup are merged at the end (shuffles within a wave, LDS across
-// waves).
+// waves). The unit's page indices are staged in LDS first, so each step's address
+// needs no global load, and K/V are read with non-temporal loads.
 #include "device.h"
 #include "kernels.h"
+#include "partition.h"
 
 namespace xattn {
 
 namespace {
 
+// 16-byte load of K/V data that is read exactly once: a non-temporal (streaming) load,
+// so the pass over the cache does not displace anything that is reused
+__device__ __forceinline__ uint4 load16(const uint4* ptr) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr)));
+}
+
 constexpr int kWaves = 4;
 constexpr int kLanesPerKey = 8;
 constexpr int kKeysPerStep = 64 / kLanesPerKey;  // keys per wave per step
-constexpr int kSteps = 4;                        // steps per loop iteration
-constexpr int kKeysPerIter = kWaves * kSteps * kKeysPerStep;
+constexpr int kSteps = 4;  // steps per loop iteration
 
 template <int D, int R>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   constexpr int CPL = D / (8 * kLanesPerKey);  // 16-byte chunks per lane per key
   constexpr int DPL = CPL * 8;                 // dims per lane
+  constexpr int kKeysPerIter = kWaves * kSteps * kKeysPerStep;
   __shared__ float sM[kWaves][R], sL[kWaves][R];
   __shared__ float sO[kWaves][R][D];
+  __shared__ int spg[kDecMaxPages];
 
   const int* u = p.units + static_cast<int64_t>(blockIdx.x) * 8;
   const int r = u[0], hk = u[1], row0 = u[2], nrows = u[3], kv0 = u[4], kv1 = u[5], ws_row = u[6];
@@ -60,6 +70,25 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     }
   }
 
+  // the unit's page indices, staged in LDS once (at most kDecMaxPages of them)
+  const bool paged = p.pages != nullptr;
+  auto logical_page = [&](int t) -> int {
+    return p.page_shift >= 0 ? (t >> p.page_shift) : (t / p.page_size);
+  };
+  const int lp_first = kv1 > kv0 ? logical_page(kv0) : 0;
+  if (paged && kv1 > kv0) {
+    // the partitioner keeps a unit within kDecMaxPages pages; the clamp only guards LDS
+    const int npg = min(logical_page(kv1 - 1) - lp_first + 1, kDecMaxPages);
+    for (int i = tid; i < npg; i += 256) spg[i] = p.pages[page_base + lp_first + i];
+    __syncthreads();
+  }
+  auto key_offset = [&](int t) -> int64_t {  // element offset of (key t, kv head hk, dim 0)
+    const int lp = logical_page(t);
+    const int page = paged ? spg[lp - lp_first] : page_base + lp;
+    const int slot = p.page_shift >= 0 ? (t & (p.page_size - 1)) : (t - lp * p.page_size);
+    return (static_cast<int64_t>(page) * p.page_size + slot) * p.hkv * D + static_cast<int64_t>(hk) * D;
+  };
+
   float m[R], l[R], o[R][DPL];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
@@ -77,13 +106,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       const int t = base + (s * kWaves + wave) * kKeysPerStep + kslot;
       key[s] = t;
       if (t < kv1) {
-        const int64_t off = kv_offset(kv_row(p, page_base, t), p.hkv, hk, D);
+        const int64_t off = key_offset(t);
         const uint4* k4 = reinterpret_cast<const uint4*>(kp + off);
         const uint4* v4 = reinterpret_cast<const uint4*>(vp + off);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-          kr[s][i] = k4[csub + kLanesPerKey * i];
-          vr[s][i] = v4[csub + kLanesPerKey * i];
+          kr[s][i] = load16(k4 + csub + kLanesPerKey * i);
+          vr[s][i] = load16(v4 + csub + kLanesPerKey * i);
         }
       } else {
 #pragma unroll

@@ -260,6 +260,7 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
     if (fam == FAM_F32) c = std::min<int64_t>(c, kF32MaxChunk);
     // a paged MFMA unit stages its page indices in LDS: keep its span within kMmaMaxPages
     if (fam == FAM_MMA && !s.identity) c = std::min<int64_t>(c, static_cast<int64_t>(kMmaMaxPages - 2) * a.page_size);
+    if (fam == FAM_DEC && !s.identity) c = std::min<int64_t>(c, static_cast<int64_t>(kDecMaxPages - 2) * a.page_size);
     c = std::min<int64_t>(std::max<int64_t>(c, 1), INT32_MAX);
     chunk[fam] = c;
     s.chunk[fam] = static_cast<int32_t>(c);

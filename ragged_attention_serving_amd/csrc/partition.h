@@ -18,6 +18,8 @@ constexpr int kMmaRows = 128;  // MFMA kernel, default: 4 waves x 32 query colum
 constexpr int kF32MaxChunk = 1024;
 // MFMA kernel: page indices of one unit staged in LDS; a unit may span at most this many pages
 constexpr int kMmaMaxPages = 1024;
+// decode kernel: page indices of one unit staged in LDS; a unit may span at most this many
+constexpr int kDecMaxPages = 2048;
 // XCDs of an MI355X: workgroup i of a launch is dispatched to XCD i % kXcds
 constexpr int kXcds = 8;
 

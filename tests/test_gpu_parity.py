@@ -250,3 +250,43 @@ def test_tile_kernel_variants(rows, gpu, monkeypatch):
         _full(w, gpu, 130)
     w = synth.ragged_case([700, 65, 300], 2, 128, block_size=64, seed=12, name="block_causal_small")
     _full(w, gpu, 0)
+
+
+def test_runs_and_plans_on_several_streams(gpu):
+    """Runs on streams other than the plan's, and a plan that moves to another stream,
+    still see their own schedule and leave the other slot's runs intact."""
+    import torch
+    import ragged_attention_serving_amd as xa
+    from tests.gpu_util import from_device
+    wa = synth.paged_case([1, 30], [700, 300], 4, 2, 64, 16, mask_mode=1, seed=20)
+    wb = synth.paged_case([5, 1, 2], [20, 900, 64], 4, 2, 64, 16, mask_mode=1, seed=21)
+    ta = [to_device(x, "bf16", gpu) for x in (wa.q, wa.k_pages, wa.v_pages)]
+    tb = [to_device(x, "bf16", gpu) for x in (wb.q, wb.k_pages, wb.v_pages)]
+    main = torch.cuda.current_stream()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(main)
+    s2.wait_stream(main)
+    plan = xa.Plan()
+    plan.plan(wa.qo_indptr, wa.kv_indptr, wa.kv_page_indices, wa.kv_last_page_len, 4, 2, 64, 16, wa.num_pages, 1,
+              stream=main)
+    outs = []
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            o, l = plan.run(*ta, stream=st)
+        outs.append((o, l))
+    # the next plans move to stream s1; the first reuses nothing, the second reuses slot A
+    with torch.cuda.stream(s1):
+        plan.plan(wb.qo_indptr, wb.kv_indptr, wb.kv_page_indices, wb.kv_last_page_len, 4, 2, 64, 16,
+                  wb.num_pages, 1, stream=s1)
+        ob, lb = plan.run(*tb, stream=s1)
+        plan.plan(wa.qo_indptr, wa.kv_indptr, wa.kv_page_indices, wa.kv_last_page_len, 4, 2, 64, 16,
+                  wa.num_pages, 1, stream=s1)
+        oc, lc = plan.run(*ta, stream=s1)
+    torch.cuda.synchronize()
+    ra, rla = ref.run_workload(wa)
+    rb, rlb = ref.run_workload(wb)
+    for i, (o, l) in enumerate(outs):
+        compare(from_device(o), l.cpu().numpy().astype(np.float64), ra, rla, "bf16", label=f"A on stream {i + 1}")
+    compare(from_device(ob), lb.cpu().numpy().astype(np.float64), rb, rlb, "bf16", label="B on s1")
+    compare(from_device(oc), lc.cpu().numpy().astype(np.float64), ra, rla, "bf16", label="A again on s1")
+    plan.close()

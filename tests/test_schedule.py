@@ -188,3 +188,18 @@ def test_short_requests_ride_with_prefill():
     assert info["num_units"][1] == 0 and info["num_units"][2] > 0
     info, units, _ = check_schedule([1] * 30 + [20], [1500] * 31, 4, 4, 16, 0, 0, "bf16")
     assert info["num_units"][1] > 0 and info["num_units"][2] > 0
+
+
+@pytest.mark.parametrize("ps,chunk", [(1, 0), (1, 9000), (16, 0), (16, 100000)])
+def test_decode_units_stay_within_the_page_cap(ps, chunk):
+    """A paged decode unit stages its page indices in LDS: it may span at most 2048 pages."""
+    kv = [40000, 3000, 70000] if ps > 1 else [9000, 2500, 5000]
+    kv_indptr, idx, last, total = synth.page_table(kv, ps, None)
+    info, units, _ = xa.xattn_schedule(synth.indptr([1, 1, 1]), kv_indptr, idx, last, 4, 4, 64, ps, total, 0, 0,
+                                       "bf16", chunk)
+    assert info["num_units"][1] == len(units) > 0
+    for u in units:
+        kv0, kv1 = int(u[4]), int(u[5])
+        if kv1 > kv0:
+            assert (kv1 - 1) // ps - kv0 // ps + 1 <= 2048, (kv0, kv1)
+    check_schedule([1, 1, 1], kv, 4, 4, ps, 0, 0, "bf16", force_chunk=chunk)

@@ -39,7 +39,7 @@ KERNEL_SOURCES = {
     "fp32": "ragged_attention_serving_amd/csrc/attn_f32.hip",
     "merge": "ragged_attention_serving_amd/csrc/merge.hip",
 }
-TIMING_EVERY = 5  # kernel events on every 5th timed run (a pair of events costs several us)
+TIMING_EVERY = 5  # kernel start/end events on every 5th timed run
 KERNEL_NAMES = {"decode": "attn_decode_kernel", "mfma": "attn_mma_kernel", "fp32": "attn_f32_kernel",
                 "merge": "merge_kernel"}
 
@@ -92,8 +92,9 @@ def measure(w, steps, warmup, dev, cold_steps=5):
         plan.run(q, k, v, out, lse)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` runs, synchronised on both sides; HIP events around the
-    # kernels of every TIMING_EVERY-th run give the per-kernel durations
+    # timed region: exactly `steps` runs, synchronised on both sides; on every TIMING_EVERY-th
+    # run the library launches each kernel with HIP events stamped with its start and end,
+    # on the run's stream, which give the per-kernel durations
     plan.set_timing(TIMING_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -204,6 +205,11 @@ def main():
     ap.add_argument("--all", action="store_true", help="also measure every other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="runs timed one by one after a 1 GiB cache flush (0: none)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device to device once (the known-size kernel that scales "
+                         "the FETCH_SIZE and WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -214,10 +220,18 @@ def main():
     from ragged_attention_serving_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4}), flush=True)
+        return
     log(f"[bench] generating {args.workload}")
     w = synth.WORKLOADS[args.workload](0)
     log(f"[bench] measuring {args.workload}: steps={args.steps} warmup={args.warmup}")
-    m = measure(w, args.steps, args.warmup, dev)
+    m = measure(w, args.steps, args.warmup, dev, args.cold_steps)
     res = summarize(w, m)
     log(f"[bench] {json.dumps({k: v for k, v in res.items() if k != 'schedule'})}")
 

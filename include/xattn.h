@@ -188,9 +188,10 @@ XATTN_API int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info);
 
 /*
  * Kernel timing. With every > 0, every `every`-th later xattn_run on this handle
- * records a pair of HIP events around each kernel it launches, on the run's stream (at
- * most 65536 pairs are kept; later runs are not recorded until the next collection).
- * Sampling keeps the cost of the events (a few microseconds per pair) off most runs.
+ * launches each kernel with a pair of HIP events that the runtime stamps with that
+ * kernel's own start and end on the run's stream (hipExtLaunchKernel; at most 65536
+ * pairs are kept; later runs are not recorded until the next collection). Sampling
+ * keeps the small cost of the events off most runs.
  * xattn_plan_timing waits for the recorded events, writes the summed milliseconds
  * and the launch count per stage {0 fp32, 1 bf16 decode, 2 bf16 MFMA tile, 3 merge}
  * into ms[4] and launches[4], and clears the records. every <= 0 stops recording.

@@ -373,37 +373,39 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
     }
     return hipEventCreate(ev);
   };
-  TimingRec rec{};
-  auto begin = [&](int stage) -> hipError_t {
+  // the runtime stamps the events with the kernel's own start and end (Launch)
+  auto launch_for = [&](xattn::Launch& l) -> hipError_t {
+    l.stream = strm;
     if (!timed) return hipSuccess;
-    rec.stage = stage;
-    hipError_t r = event(&rec.start);
-    if (r == hipSuccess) r = event(&rec.stop);
-    if (r == hipSuccess) r = hipEventRecord(rec.start, strm);
+    hipError_t r = event(&l.start);
+    if (r == hipSuccess) r = event(&l.stop);
     return r;
   };
-  auto end = [&]() -> hipError_t {
-    if (!timed) return hipSuccess;
-    const hipError_t r = hipEventRecord(rec.stop, strm);
-    if (r == hipSuccess) plan->timing_recs.push_back(rec);
-    return r;
+  auto launched = [&](int stage, const xattn::Launch& l) {
+    if (timed) plan->timing_recs.push_back(TimingRec{stage, l.start, l.stop});
+  };
+  auto unused = [&](const xattn::Launch& l) {  // a failed launch hands its events back
+    if (l.start) plan->event_pool.push_back(l.start);
+    if (l.stop) plan->event_pool.push_back(l.stop);
   };
 
   for (int f = 0; f < xattn::FAM_COUNT; ++f) {
     if (s.units[f].empty()) continue;
     p.units = dev + sl.off_units[f];
     p.num_units = static_cast<int32_t>(s.units[f].size());
-    if ((e = begin(f)) != hipSuccess) return hip_err(e, "timing event");
-    if (f == xattn::FAM_F32) e = xattn::launch_attn_f32(p, strm);
-    else if (f == xattn::FAM_DEC) e = xattn::launch_attn_decode(p, s.dec_rows, strm);
-    else e = xattn::launch_attn_mma(p, strm);
-    if (e != hipSuccess) return hip_err(e, "attention kernel launch");
-    if ((e = end()) != hipSuccess) return hip_err(e, "timing event");
+    xattn::Launch l;
+    if ((e = launch_for(l)) != hipSuccess) return unused(l), hip_err(e, "timing event");
+    if (f == xattn::FAM_F32) e = xattn::launch_attn_f32(p, l);
+    else if (f == xattn::FAM_DEC) e = xattn::launch_attn_decode(p, s.dec_rows, l);
+    else e = xattn::launch_attn_mma(p, l);
+    if (e != hipSuccess) return unused(l), hip_err(e, "attention kernel launch");
+    launched(f, l);
   }
   if (!s.merges.empty()) {
-    if ((e = begin(3)) != hipSuccess) return hip_err(e, "timing event");
-    if ((e = xattn::launch_merge(p, sl.dtype, strm)) != hipSuccess) return hip_err(e, "merge kernel launch");
-    if ((e = end()) != hipSuccess) return hip_err(e, "timing event");
+    xattn::Launch l;
+    if ((e = launch_for(l)) != hipSuccess) return unused(l), hip_err(e, "timing event");
+    if ((e = xattn::launch_merge(p, sl.dtype, l)) != hipSuccess) return unused(l), hip_err(e, "merge kernel launch");
+    launched(3, l);
   }
   if (stream != sl.plan_stream) {
     // not ordered before the slot's next copy by the stream: fence this stream

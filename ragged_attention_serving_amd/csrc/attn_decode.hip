@@ -239,25 +239,24 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
 }
 
 template <int D>
-hipError_t launch_rows(const AttnParams& p, int rows, hipStream_t stream) {
+hipError_t launch_rows(const AttnParams& p, int rows, const Launch& l) {
   const dim3 grid(p.num_units), block(256);
   switch (rows) {
-    case 1: hipLaunchKernelGGL((attn_decode_kernel<D, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((attn_decode_kernel<D, 2>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((attn_decode_kernel<D, 4>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((attn_decode_kernel<D, 8>), grid, block, 0, stream, p); break;
+    case 1: return launch_kernel(attn_decode_kernel<D, 1>, grid, block, p, l);
+    case 2: return launch_kernel(attn_decode_kernel<D, 2>, grid, block, p, l);
+    case 4: return launch_kernel(attn_decode_kernel<D, 4>, grid, block, p, l);
+    case 8: return launch_kernel(attn_decode_kernel<D, 8>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_decode(const AttnParams& p, int rows, hipStream_t stream) {
+hipError_t launch_attn_decode(const AttnParams& p, int rows, const Launch& l) {
   if (p.num_units == 0) return hipSuccess;
   switch (p.d) {
-    case 64: return launch_rows<64>(p, rows, stream);
-    case 128: return launch_rows<128>(p, rows, stream);
+    case 64: return launch_rows<64>(p, rows, l);
+    case 128: return launch_rows<128>(p, rows, l);
     default: return hipErrorInvalidValue;
   }
 }

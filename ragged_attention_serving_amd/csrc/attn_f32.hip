@@ -122,17 +122,16 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
 
 }  // namespace
 
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_f32(const AttnParams& p, const Launch& l) {
   if (p.num_units == 0) return hipSuccess;
   const dim3 grid(p.num_units), block(256);
   switch (p.d) {
-    case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, block, 0, stream, p); break;
+    case 16: return launch_kernel(attn_f32_kernel<16>, grid, block, p, l);
+    case 32: return launch_kernel(attn_f32_kernel<32>, grid, block, p, l);
+    case 64: return launch_kernel(attn_f32_kernel<64>, grid, block, p, l);
+    case 128: return launch_kernel(attn_f32_kernel<128>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace xattn

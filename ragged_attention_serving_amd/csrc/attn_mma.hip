@@ -318,31 +318,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
 }
 
 template <int D, int NW>
-hipError_t launch_dw(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_dw(const AttnParams& p, const Launch& l) {
   const dim3 grid(p.num_units), block(64 * NW);
   switch (p.mask) {
-    case 0: hipLaunchKernelGGL((attn_mma_kernel<D, 0, NW>), grid, block, 0, stream, p); break;
-    case 1: hipLaunchKernelGGL((attn_mma_kernel<D, 1, NW>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((attn_mma_kernel<D, 2, NW>), grid, block, 0, stream, p); break;
+    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW>, grid, block, p, l);
+    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW>, grid, block, p, l);
+    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const AttnParams& p, hipStream_t stream) {
-  if (p.tile_rows == 128) return launch_dw<D, 4>(p, stream);
-  if (p.tile_rows == 256) return launch_dw<D, 8>(p, stream);
+hipError_t launch_d(const AttnParams& p, const Launch& l) {
+  if (p.tile_rows == 128) return launch_dw<D, 4>(p, l);
+  if (p.tile_rows == 256) return launch_dw<D, 8>(p, l);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_attn_mma(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attn_mma(const AttnParams& p, const Launch& l) {
   if (p.num_units == 0) return hipSuccess;
   switch (p.d) {
-    case 64: return launch_d<64>(p, stream);
-    case 128: return launch_d<128>(p, stream);
+    case 64: return launch_d<64>(p, l);
+    case 128: return launch_d<128>(p, l);
     default: return hipErrorInvalidValue;
   }
 }

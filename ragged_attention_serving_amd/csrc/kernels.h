@@ -7,13 +7,29 @@
 
 namespace xattn {
 
+// Where a kernel goes: the stream and, when timing, two events that the runtime stamps
+// with the kernel's own start and end (hipExtLaunchKernel), so that the measured time is
+// the kernel's alone, with no launch gap.
+struct Launch {
+  hipStream_t stream = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename Kernel>
+hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, const AttnParams& p, const Launch& l) {
+  void* args[] = {const_cast<AttnParams*>(&p)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, l.stream,
+                            l.start, l.stop, 0);
+}
+
 // fp32 storage and arithmetic, any mask, head_dim 16/32/64/128; units of <= 4 rows.
-hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, const Launch& l);
 // bf16 decode: units of up to `rows` query rows sharing one KV head (rows in 1,2,4,8).
-hipError_t launch_attn_decode(const AttnParams& p, int rows, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnParams& p, int rows, const Launch& l);
 // bf16 MFMA tiles: units of up to 128 query rows sharing one KV head.
-hipError_t launch_attn_mma(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_mma(const AttnParams& p, const Launch& l);
 // log-sum-exp merge of split rows into out (dtype 0 fp32, 1 bf16) and lse.
-hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t stream);
+hipError_t launch_merge(const AttnParams& p, int dtype, const Launch& l);
 
 }  // namespace xattn

@@ -55,23 +55,22 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 }
 
 template <bool BF16>
-hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_t(const AttnParams& p, const Launch& l) {
   const dim3 grid((p.num_merges + 3) / 4), block(256);
   switch (p.d) {
-    case 16: hipLaunchKernelGGL((merge_kernel<16, BF16>), grid, block, 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((merge_kernel<32, BF16>), grid, block, 0, stream, p); break;
-    case 64: hipLaunchKernelGGL((merge_kernel<64, BF16>), grid, block, 0, stream, p); break;
-    case 128: hipLaunchKernelGGL((merge_kernel<128, BF16>), grid, block, 0, stream, p); break;
+    case 16: return launch_kernel(merge_kernel<16, BF16>, grid, block, p, l);
+    case 32: return launch_kernel(merge_kernel<32, BF16>, grid, block, p, l);
+    case 64: return launch_kernel(merge_kernel<64, BF16>, grid, block, p, l);
+    case 128: return launch_kernel(merge_kernel<128, BF16>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_merge(const AttnParams& p, int dtype, hipStream_t stream) {
+hipError_t launch_merge(const AttnParams& p, int dtype, const Launch& l) {
   if (p.num_merges == 0) return hipSuccess;
-  return dtype == 1 ? launch_t<true>(p, stream) : launch_t<false>(p, stream);
+  return dtype == 1 ? launch_t<true>(p, l) : launch_t<false>(p, l);
 }
 
 }  // namespace xattn

@@ -62,8 +62,10 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
+    # -z defs: a symbol left undefined (a kernel whose launch stub a compilation pass did
+    # not emit, say) fails the link here instead of the library's first load
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
-          f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+          f"-L{ROCM}/lib", "-lamdhip64", f"-Wl,-rpath,{ROCM}/lib", "-Wl,-z,defs"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

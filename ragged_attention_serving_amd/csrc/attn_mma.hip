@@ -34,21 +34,22 @@ namespace xattn {
 
 namespace {
 
-constexpr int kBN = 64;  // keys per tile
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-template <int D, int NW>
+template <int D, int NW, int BN>
 struct Cfg {
   static constexpr int THREADS = 64 * NW;
+  static constexpr int NKB = BN / 32;          // 32-key blocks per tile
+  static constexpr int NST = BN / 16;          // 16-key MFMA k-steps of P V per tile
   static constexpr int ROWB = 2 * D;           // bytes per key row
   static constexpr int RPI = 1024 / ROWB;      // key rows per 1 KB load instruction
   static constexpr int LPR = 64 / RPI;         // lanes per key row in a load
-  static constexpr int NIW = kBN / RPI / NW;   // load instructions per wave per tile (K or V)
-  static_assert(NIW * RPI * NW == kBN, "tile split across waves");
-  static constexpr int TILE = kBN * ROWB;      // bytes of one K (or V) tile
+  static constexpr int NIW = BN / RPI / NW;    // load instructions per wave per tile (K or V)
+  static_assert(NIW * RPI * NW == BN, "tile split across waves");
+  static constexpr int TILE = BN * ROWB;       // bytes of one K (or V) tile
   // 16-byte chunk swizzle: chunk c of key row r is stored in slot c ^ swz(r). With 64
   // banks of 4 bytes (a 256-byte window; a D=128 row fills one, a D=64 row half of one):
   //  * the K operand read has 16 lanes on 16 consecutive rows at one chunk: swz takes 16
@@ -71,9 +72,10 @@ __device__ __forceinline__ void block_barrier() {
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-template <int D, int MASK, int NW>
+template <int D, int MASK, int NW, int BN>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p) {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, BN>;
+  constexpr int NKB = C::NKB, NST = C::NST;
   constexpr int NKK = D / 16;  // MFMA k-steps for Q.K^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
   // one LDS object per buffer: the compiler then knows which buffer every global->LDS
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   }
   const int lim = valid ? min(last_visible(MASK, p.block, qo_len, kv_len, qi), kv1 - 1) : kv1 - 1;
 
-  const int ntiles = kv1 > kv0 ? (kv1 - kv0 + kBN - 1) / kBN : 0;
+  const int ntiles = kv1 > kv0 ? (kv1 - kv0 + BN - 1) / BN : 0;
   const bool paged = p.pages != nullptr;
 
   // ---- the unit's page indices, staged in LDS once (at most kMmaMaxPages of them)
@@ -128,25 +130,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   // ---- pool (row, head) index of key `lane` of tile j (keys past the range clamp to its
   // last key, whose scores are masked)
   auto tile_row_head = [&](int j) __attribute__((always_inline)) -> int {
-    const int t = min(kv0 + j * kBN + lane, kv1 - 1);
+    const int t = min(kv0 + j * BN + lane, kv1 - 1);
     const int lp = logical_page(t);
     const int page = paged ? spg[lp - lp_first] : page_base + lp;
     const int slot = p.page_shift >= 0 ? (t & (p.page_size - 1)) : (t - lp * p.page_size);
     return (page * p.page_size + slot) * p.hkv + hk;
   };
-  // ---- global -> LDS loads of one tile j of `src` into `dst` (this wave's share); the
-  // pool row of each key comes from lane `key` of the tile's row ids
-  auto issue = [&](const char* src, lds_char* dst, int j) __attribute__((always_inline)) {
+  // ---- global -> LDS loads of tile j: this wave fills NIW 1 KB blocks of the K tile and
+  // the same blocks of the V tile. The byte offsets in the pool (shared by K and V) come
+  // from the tile's row ids, the row of key k being held by lane k.
+  struct TileOffsets {
+    int64_t v[C::NIW];
+  };
+  auto tile_offsets = [&](int j) __attribute__((always_inline)) -> TileOffsets {
     const int rh = tile_row_head(j);
+    TileOffsets t;
 #pragma unroll
     for (int i = 0; i < C::NIW; ++i) {
       const int n = C::NIW * wave + i;             // 1 KB block of the tile
       const int key = C::RPI * n + lane / C::LPR;  // key row this lane fills
       const int src16 = (lane % C::LPR) ^ C::swz(key);  // global chunk for this slot
-      const int64_t row_head = __shfl(rh, key, 64);
-      const int64_t off = row_head * C::ROWB + 16 * src16;
-      __builtin_amdgcn_global_load_lds(src + off, dst + n * 1024, 16, 0, 0);
+      t.v[i] = static_cast<int64_t>(__shfl(rh, key, 64)) * C::ROWB + 16 * src16;
     }
+    return t;
+  };
+  auto issue_one = [&](const char* src, lds_char* dst, const TileOffsets& t, int i) __attribute__((always_inline)) {
+    // (both addresses are variables of their own: with template-dependent expressions in
+    // the builtin's arguments, the host compilation pass silently drops the kernel's
+    // launch stub)
+    const int n = C::NIW * wave + i;
+    const char* g = src + t.v[i];
+    __builtin_amdgcn_global_load_lds(g, dst + n * 1024, 16, 0, 0);
+  };
+  auto issue = [&](const char* src, lds_char* dst, int j) __attribute__((always_inline)) {
+    const TileOffsets t = tile_offsets(j);
+#pragma unroll
+    for (int i = 0; i < C::NIW; ++i) issue_one(src, dst, t, i);
   };
 
   // ---- per-lane LDS read offsets (bytes within a buffer), fixed for the unit.
@@ -178,12 +197,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   float m = -INFINITY, lsum = 0.f;
 
   // max over a lane's query column: its 32 accumulators, then the 32 in lane ^ 32
-  auto column_max = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) -> float {
+  auto column_max = [&](const f32x16_t (&s)[NKB]) __attribute__((always_inline)) -> float {
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    for (int kb = 1; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     return fmaxf(mx, shfl_xor_f(mx, 32));
   };
 
@@ -202,35 +223,80 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     constexpr int P = decltype(par)::value;
     lds_char* kcur = (lds_char*)(P == 0 ? sk0 : sk1);
     lds_char* vcur = (lds_char*)(P == 0 ? sv0 : sv1);
-    if (j + 1 < ntiles) {
-      issue(kbytes, (lds_char*)(P == 0 ? sk1 : sk0), j + 1);
-      issue(vbytes, (lds_char*)(P == 0 ? sv1 : sv0), j + 1);
+    lds_char* knext = (lds_char*)(P == 0 ? sk1 : sk0);
+    lds_char* vnext = (lds_char*)(P == 0 ? sv1 : sv0);
+    const bool more = j + 1 < ntiles;
+    TileOffsets nxt{};
+    if (more) nxt = tile_offsets(j + 1);
+    if (!wave_active && more) {
+#pragma unroll
+      for (int i = 0; i < C::NIW; ++i) issue_one(kbytes, knext, nxt, i);
+#pragma unroll
+      for (int i = 0; i < C::NIW; ++i) issue_one(vbytes, vnext, nxt, i);
     }
     if (wave_active) {
-      // S^T = K Q^T for the tile's two 32-key blocks; accumulator i of block kb holds
-      // key 32kb + 8(i/4) + 4half + i%4 of the tile
-      f32x16_t sc[2];
+      // S^T = K Q^T for the tile's 32-key blocks; accumulator i of block kb holds key
+      // 32kb + 8(i/4) + 4half + i%4 of the tile. All K fragments of the tile are read
+      // first, so their LDS latencies overlap; the blocks' MFMA chains then interleave.
+      bf16x8_t ka[NKB][NKK];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          ka[kb][kk] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+              kcur + koff[kk] + 32 * kb * C::ROWB);
+      f32x16_t sc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
+      // the next tile's loads go out one at a time between the MFMAs, so that no wave
+      // waits at a full address queue before it can compute
+      static_assert(NKK % (2 * C::NIW) == 0 || (2 * C::NIW) % NKK == 0, "load spread");
+      constexpr int PER_KK = (2 * C::NIW + NKK - 1) / NKK;  // loads after each k-step
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-              kcur + koff[kk] + 32 * kb * C::ROWB);
-          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[kk], sc[kb], 0, 0, 0);
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][kk], qb[kk], sc[kb], 0, 0, 0);
+        if (more) {
+#pragma unroll
+          for (int x = 0; x < PER_KK; ++x) {
+            const int i = kk * PER_KK + x;
+            if (i < C::NIW) issue_one(kbytes, knext, nxt, i);
+            else if (i < 2 * C::NIW) issue_one(vbytes, vnext, nxt, i - C::NIW);
+          }
         }
       }
 
-      const int t0 = kv0 + j * kBN;
-      if (__any(t0 + kBN - 1 > lim)) {
+      // V^T fragments for P V, read now so that they arrive while the softmax runs.
+      // k-step st4 covers keys 16st4 + [0, 16): this lane's 8 are 16st4 + 4half + {0..3}
+      // and 16st4 + 8 + 4half + {0..3}. The transpose read of a 16-lane group whose lane
+      // i addresses key kbase + i/4, dims dbase + 4(i%4) .. +3 returns to lane i dim
+      // dbase + i of keys kbase .. kbase + 3.
+      bf16x8_t va[NDB][NST];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int t = t0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
-            if (t > lim) sc[kb][i] = -INFINITY;
-          }
+        for (int st4 = 0; st4 < NST; ++st4) {
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) short4_t*>(vcur + voff[db][0] + 16 * st4 * C::ROWB));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) short4_t*>(vcur + voff[db][1] + 16 * st4 * C::ROWB));
+          const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          va[db][st4] = __builtin_bit_cast(bf16x8_t, a8);
+        }
+
+      // keys past the last one this query sees: key 32kb + 8(i/4) + 4half + i%4 is
+      // visible iff 32kb + 8(i/4) + i%4 <= lim - t0 - 4half (a compare with a constant)
+      const int t0 = kv0 + j * BN;
+      if (__any(t0 + BN - 1 > lim)) {
+        const int d = lim - t0 - 4 * half;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kb + 8 * (i / 4) + (i % 4) > d) sc[kb][i] = -INFINITY;
       }
       const float mxs = column_max(sc) * p.scale_log2;
       if (__any(mxs > m + kRescaleSlack)) {
@@ -246,9 +312,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
       const float mu = m == -INFINITY ? 0.f : m;
 
       // probabilities, row sums, and the bf16 B operands for P V (k-step = 16 keys)
-      bf16x8_t pb[4];
+      bf16x8_t pb[NST];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < NST; ++b) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -260,22 +326,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
         pb[b] = __builtin_bit_cast(bf16x8_t, packed);
       }
 
-      // O^T += V^T P^T. k-step st4 covers keys 16st4 + [0, 16): this lane's 8 are
-      // 16st4 + 4half + {0..3} and 16st4 + 8 + 4half + {0..3}. The transpose read of a
-      // 16-lane group whose lane i addresses key kbase + i/4, dims dbase + 4(i%4) .. +3
-      // returns to lane i dim dbase + i of keys kbase .. kbase + 3.
+      // O^T += V^T P^T
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int st4 = 0; st4 < NST; ++st4)
 #pragma unroll
-        for (int st4 = 0; st4 < 4; ++st4) {
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<__attribute__((address_space(3))) short4_t*>(vcur + voff[db][0] + 16 * st4 * C::ROWB));
-          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<__attribute__((address_space(3))) short4_t*>(vcur + voff[db][1] + 16 * st4 * C::ROWB));
-          const short __attribute__((ext_vector_type(8))) a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pb[st4], o[db], 0, 0, 0);
-        }
-      }
+        for (int db = 0; db < NDB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][st4], pb[st4], o[db], 0, 0, 0);
     }
     wait_all_loads();
     block_barrier();
@@ -317,21 +373,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int BN>
 hipError_t launch_dw(const AttnParams& p, const Launch& l) {
   const dim3 grid(p.num_units), block(64 * NW);
   switch (p.mask) {
-    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW>, grid, block, p, l);
-    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW>, grid, block, p, l);
-    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW>, grid, block, p, l);
+    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW, BN>, grid, block, p, l);
+    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW, BN>, grid, block, p, l);
+    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW, BN>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
 }
 
+constexpr int kTileKeys = 64;  // keys per K/V tile
+
 template <int D>
 hipError_t launch_d(const AttnParams& p, const Launch& l) {
-  if (p.tile_rows == 128) return launch_dw<D, 4>(p, l);
-  if (p.tile_rows == 256) return launch_dw<D, 8>(p, l);
+  if (p.tile_rows == 128) return launch_dw<D, 4, kTileKeys>(p, l);
+  if (p.tile_rows == 256) return launch_dw<D, 8, 64>(p, l);
   return hipErrorInvalidValue;
 }
 

@@ -87,7 +87,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   const int r = u[0], hk = u[1], row0 = u[2], nrows = u[3], kv0 = u[4], kv1 = u[5], ws_row = u[6];
   const int* rq = p.reqs + 4 * r;
   const int qo_start = rq[0], qo_len = rq[1], kv_len = rq[2], page_base = rq[3];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave math scalar
   const int col = lane & 31, half = lane >> 5;
   const int g = p.group;
   const char* kbytes = static_cast<const char*>(p.k);
@@ -127,8 +128,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     __syncthreads();
   }
 
-  // ---- pool (row, head) index of key `lane` of tile j (keys past the range clamp to its
-  // last key, whose scores are masked)
+  // ---- paged table: pool (row, head) index of key `lane` of tile j (keys past the range
+  // clamp to its last key, whose scores are masked)
   auto tile_row_head = [&](int j) __attribute__((always_inline)) -> int {
     const int t = min(kv0 + j * BN + lane, kv1 - 1);
     const int lp = logical_page(t);
@@ -142,15 +143,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   struct TileOffsets {
     int64_t v[C::NIW];
   };
-  auto tile_offsets = [&](int j) __attribute__((always_inline)) -> TileOffsets {
-    const int rh = tile_row_head(j);
+  // identity table: key t of the request is pool row page_base * page_size + t, so a
+  // lane's offsets for tile j are those of tile 0 plus j whole tiles, except in a last
+  // tile that runs past the range (its keys clamp to the range's last key)
+  TileOffsets id_base;
+  const int64_t id_stride = static_cast<int64_t>(BN) * p.hkv * C::ROWB;
+  auto identity_offsets = [&](int j) __attribute__((always_inline)) -> TileOffsets {
     TileOffsets t;
 #pragma unroll
     for (int i = 0; i < C::NIW; ++i) {
       const int n = C::NIW * wave + i;             // 1 KB block of the tile
       const int key = C::RPI * n + lane / C::LPR;  // key row this lane fills
       const int src16 = (lane % C::LPR) ^ C::swz(key);  // global chunk for this slot
-      t.v[i] = static_cast<int64_t>(__shfl(rh, key, 64)) * C::ROWB + 16 * src16;
+      const int row = (page_base * p.page_size + min(kv0 + j * BN + key, kv1 - 1)) * p.hkv + hk;
+      t.v[i] = static_cast<int64_t>(static_cast<uint32_t>(row)) * C::ROWB + 16 * src16;
+    }
+    return t;
+  };
+  if (!paged) id_base = identity_offsets(0);
+  auto tile_offsets = [&](int j) __attribute__((always_inline)) -> TileOffsets {
+    TileOffsets t;
+    if (!paged) {
+      if (kv0 + (j + 1) * BN > kv1) return identity_offsets(j);
+      const int64_t add = id_stride * j;
+#pragma unroll
+      for (int i = 0; i < C::NIW; ++i) t.v[i] = id_base.v[i] + add;
+      return t;
+    }
+    const int rh = tile_row_head(j);
+#pragma unroll
+    for (int i = 0; i < C::NIW; ++i) {
+      const int n = C::NIW * wave + i;
+      const int key = C::RPI * n + lane / C::LPR;
+      const int src16 = (lane % C::LPR) ^ C::swz(key);
+      t.v[i] = static_cast<int64_t>(static_cast<uint32_t>(__shfl(rh, key, 64))) * C::ROWB + 16 * src16;
     }
     return t;
   };

@@ -123,6 +123,38 @@ def measure(w, steps, warmup, dev, cold_steps=5):
                 cold_ms=float(np.median(cold)) if cold else None)
 
 
+def measure_write(w, steps, warmup, dev):
+    """Times the context write (xattn_write_kv) of w's contexts into fresh pools: `steps`
+    back-to-back writes between two synchronisations. Bytes moved: the packed K and V
+    rows read once and written once."""
+    import torch
+    import ragged_attention_serving_amd as xa
+    from ragged_attention_serving_amd import synth
+
+    ks, vs = synth.context_source(w, seed=1)
+    ksrc, vsrc = to_dev(ks, w.dtype, dev), to_dev(vs, w.dtype, dev)
+    del ks, vs
+    kpool = torch.zeros(w.k_pages.shape, dtype=ksrc.dtype, device=dev)
+    vpool = torch.zeros(w.v_pages.shape, dtype=ksrc.dtype, device=dev)
+    plan = xa.Plan()
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, w.num_qo_heads,
+              w.num_kv_heads, w.head_dim, w.page_size, w.num_pages, w.mask_mode, w.block_size,
+              w.sm_scale, w.dtype)
+    for _ in range(warmup):
+        plan.write_kv(ksrc, vsrc, kpool, vpool)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.write_kv(ksrc, vsrc, kpool, vpool)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    moved = 2 * 2 * ksrc.numel() * ksrc.element_size()
+    plan.close()
+    return {"workload": f"context_write:{w.name}", "ms_per_write": round(ms, 5),
+            "bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
+            "hbm_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def summarize(w, m):
     kv_bytes, flops, decode = workload_numbers(w, m["info"])
     per = {}
@@ -285,6 +317,10 @@ def main():
             log(f"[bench] {json.dumps(r)}")
             del ws, ms
             torch.cuda.empty_cache()
+        log("[bench] sweep: context write")
+        wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), max(5, min(args.steps, 20)), 3, dev)
+        sweep[wr["workload"]] = wr
+        log(f"[bench] {json.dumps(wr)}")
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)
 

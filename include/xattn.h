@@ -145,6 +145,32 @@ XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int
 XATTN_API int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
               void* out, float* lse, void* stream);
 
+/*
+ * xattn_write_kv: the step before the path. Writes each request's context keys and
+ * values into its pages once, so that later runs read them (page
+ * "mstar.engine.resources.attn.cross": the context is written once by the encode step
+ * and then read as an ordinary paged KV stream; page "mstar.model.components.attention",
+ * CrossAttention.compute_kv: a request's keys and values come out as (length, heads,
+ * head_dim)). Uses the page table of the latest schedule.
+ *
+ * k_src, v_src      device [sum kv_len, Hkv, D] in the plan's dtype, requests packed in
+ *                   order (request r's rows start at kv_len[0] + ... + kv_len[r-1]),
+ *                   16-byte aligned; not written.
+ * k_pages, v_pages  device pools [num_pages, page_size, Hkv, D], 16-byte aligned.
+ *                   Position t of request r goes to slot t % page_size of page
+ *                   kv_page_indices[kv_indptr[r] + t / page_size] (identity table:
+ *                   page kv_indptr[r] + t / page_size). Slots past a request's kv_len in
+ *                   its last page, and pages of no request, are left untouched.
+ * stream            hipStream_t; ordered with the plan's copy like xattn_run.
+ *
+ * Returns XATTN_ERR_INVALID_ARG for a handle with no schedule or a NULL or misaligned
+ * pointer, XATTN_ERR_UNSUPPORTED when the contexts hold more than 2^31-1 rows in total,
+ * XATTN_ERR_HIP for a launch failure. Pages shared by two requests are written by both,
+ * in no fixed order.
+ */
+XATTN_API int xattn_write_kv(xattn_plan_t plan, const void* k_src, const void* v_src, void* k_pages,
+                             void* v_pages, void* stream);
+
 /* 1 if the next xattn_plan on this handle (on the same stream) would not wait, 0 if it
  * would, negative on error. Never blocks. */
 XATTN_API int xattn_plan_ready(xattn_plan_t plan);

@@ -152,15 +152,22 @@ def paged_attention(q, k_pages, v_pages, qo_indptr, kv_indptr, kv_page_indices,
 
 def ragged_attention(q, k, v, cu_seqlens, num_qo_heads, num_kv_heads, *, dtype="bf16",
                      mask_mode=MASK_BLOCK_CAUSAL, block_size=64, sm_scale=0.0,
-                     requests=None, heads=None):
-    """Cacheless attention within each span of packed q/k/v ([T, H, D], spans by cu_seqlens).
+                     requests=None, heads=None, cu_seqlens_kv=None):
+    """Cacheless attention over spans of packed tensors: no page table.
 
-    Keys and values are sliced directly from the packed tensors: no page table.
+    q is [Tq, Hq, D] with request r's queries at rows cu_seqlens[r] .. cu_seqlens[r+1].
+    k and v are [Tkv, Hkv, D] (or [Tkv, 1, Hkv, D]); request r's keys are the same span
+    (self-attention within each span, page "mstar.engine.resources.attn.ragged.base",
+    RaggedAttnManager and RaggedBlockCausalAttnManager) or, with cu_seqlens_kv, the span
+    cu_seqlens_kv[r] .. cu_seqlens_kv[r+1] of a second packed tensor (cross-attention
+    between two spans of each request, RaggedCrossAttnManager on the same page). Query i
+    of a span sits at key position kv_len - qo_len + i for the causal masks.
     """
     group = num_qo_heads // num_kv_heads
     d = q.shape[-1]
     scale = sm_scale if sm_scale > 0 else 1.0 / math.sqrt(d)
     cu = np.asarray(cu_seqlens, np.int64)
+    cukv = cu if cu_seqlens_kv is None else np.asarray(cu_seqlens_kv, np.int64)
     k = k.reshape(k.shape[0] * (k.shape[1] if k.ndim == 4 else 1), num_kv_heads, d)
     v = v.reshape(v.shape[0] * (v.shape[1] if v.ndim == 4 else 1), num_kv_heads, d)
     t = int(cu[-1])
@@ -170,13 +177,14 @@ def ragged_attention(q, k, v, cu_seqlens, num_qo_heads, num_kv_heads, *, dtype="
     hs = range(num_qo_heads) if heads is None else heads
     for r in reqs:
         a, b = int(cu[r]), int(cu[r + 1])
+        ka, kb = int(cukv[r]), int(cukv[r + 1])
         if b == a:
             continue
-        vis = visible(mask_mode, b - a, b - a, block_size)
+        vis = visible(mask_mode, b - a, kb - ka, block_size)
         for h in hs:
             hk = h // group
-            o, s = attend(to_f64(q[a:b, h], dtype), to_f64(k[a:b, hk], dtype),
-                          to_f64(v[a:b, hk], dtype), vis, scale)
+            o, s = attend(to_f64(q[a:b, h], dtype), to_f64(k[ka:kb, hk], dtype),
+                          to_f64(v[ka:kb, hk], dtype), vis, scale)
             out[a:b, h] = o
             lse[a:b, h] = s
     return out, lse
@@ -201,13 +209,39 @@ def merge_states(outs, lses):
     return O, lse
 
 
+def write_context(k_src, v_src, k_pages, v_pages, kv_indptr, kv_page_indices, kv_last_page_len,
+                  page_size):
+    """The context write that precedes the path: each request's keys and values, packed
+    in request order as (length, heads, head_dim) rows, go into the slots of its pages
+    (page "mstar.engine.resources.attn.cross": the context is written once and then read
+    as a paged KV stream; page "mstar.model.components.attention", CrossAttention.compute_kv
+    gives a request's keys and values as (length, heads, head_dim)).
+
+    Position t of request r takes slot t % page_size of the page the table lists at
+    logical page t // page_size. Returns new pools; every other slot keeps its value.
+    """
+    kp, vp = np.array(k_pages, copy=True), np.array(v_pages, copy=True)
+    _, kv_len = request_lengths(np.zeros(len(kv_indptr), np.int64), kv_indptr, kv_last_page_len,
+                                page_size)
+    start = 0
+    for r in range(len(kv_indptr) - 1):
+        for t in range(int(kv_len[r])):
+            logical = int(kv_indptr[r]) + t // page_size
+            page = logical if kv_page_indices is None else int(kv_page_indices[logical])
+            kp[page, t % page_size] = k_src[start + t]
+            vp[page, t % page_size] = v_src[start + t]
+        start += int(kv_len[r])
+    return kp, vp
+
+
 def run_workload(w, requests=None, heads=None):
     """Oracle over a synth.Workload-like object (paged or cacheless)."""
     if w.kv_page_indices is None and w.page_size == 1 and "cu_seqlens" in getattr(w, "meta", {}):
         return ragged_attention(w.q, w.k_pages, w.v_pages, w.meta["cu_seqlens"], w.num_qo_heads,
                                 w.num_kv_heads, dtype=w.dtype, mask_mode=w.mask_mode,
                                 block_size=w.block_size, sm_scale=w.sm_scale,
-                                requests=requests, heads=heads)
+                                requests=requests, heads=heads,
+                                cu_seqlens_kv=w.meta.get("cu_seqlens_kv"))
     return paged_attention(w.q, w.k_pages, w.v_pages, w.qo_indptr, w.kv_indptr, w.kv_page_indices,
                            w.kv_last_page_len, w.num_qo_heads, w.num_kv_heads, w.page_size,
                            dtype=w.dtype, mask_mode=w.mask_mode, block_size=w.block_size,

@@ -32,7 +32,7 @@ XATTN_ERR_OOM = -4
 XATTN_ERR_BUSY = -5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
-EXPORTED = ("xattn_plan", "xattn_run", "xattn_plan_ready", "xattn_plan_destroy",
+EXPORTED = ("xattn_plan", "xattn_run", "xattn_write_kv", "xattn_plan_ready", "xattn_plan_destroy",
             "xattn_last_error", "xattn_schedule", "xattn_plan_info", "xattn_plan_set_timing",
             "xattn_plan_timing")
 STAGES = ("fp32", "decode", "mfma", "merge")
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.xattn_plan.restype = ctypes.c_int
     L.xattn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.xattn_run.restype = ctypes.c_int
+    L.xattn_write_kv.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.xattn_write_kv.restype = ctypes.c_int
     L.xattn_plan_ready.argtypes = [vp]
     L.xattn_plan_ready.restype = ctypes.c_int
     L.xattn_plan_destroy.argtypes = [vp]
@@ -189,6 +191,13 @@ def xattn_run(handle, q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, lse_ptr:
     _check(lib().xattn_run(handle, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr or None, _stream_handle(stream)))
 
 
+def xattn_write_kv(handle, k_src_ptr: int, v_src_ptr: int, k_pages_ptr: int, v_pages_ptr: int,
+                   stream=None) -> None:
+    """Raw context write on device pointers (ints)."""
+    _check(lib().xattn_write_kv(handle, k_src_ptr, v_src_ptr, k_pages_ptr, v_pages_ptr,
+                                _stream_handle(stream)))
+
+
 def xattn_plan_ready(handle) -> bool:
     return bool(_check(lib().xattn_plan_ready(handle)))
 
@@ -236,7 +245,8 @@ class Plan:
                    dtype, stream)
         total_q = int(np.asarray(qo_indptr)[-1]) if len(qo_indptr) else 0
         self.meta = dict(total_q=total_q, hq=num_qo_heads, hkv=num_kv_heads, d=head_dim,
-                         page_size=page_size, num_pages=int(num_pages), dtype=_dtype_code(dtype))
+                         page_size=page_size, num_pages=int(num_pages), dtype=_dtype_code(dtype),
+                         total_kv=int(xattn_plan_info(self._h)["total_kv_tokens"]))
         return self
 
     def run(self, q, k_pages, v_pages, out=None, lse=None, stream=None, want_lse=True):
@@ -264,6 +274,28 @@ class Plan:
         xattn_run(self._h, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
                   lse.data_ptr() if lse is not None else None, stream)
         return out, lse
+
+    def write_kv(self, k_src, v_src, k_pages, v_pages, stream=None):
+        """Writes the planned requests' packed context rows (k_src/v_src [sum kv_len, Hkv, D])
+        into their page slots of k_pages/v_pages (CUDA tensors of the planned dtype)."""
+        import torch
+        if self.meta is None:
+            raise XattnError(XATTN_ERR_INVALID_ARG, "write_kv before plan")
+        m = self.meta
+        tdt = torch.float32 if m["dtype"] == F32 else torch.bfloat16
+        rows = m["total_kv"]
+        for name, t in (("k_src", k_src), ("v_src", v_src), ("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous CUDA {tdt} tensor")
+        for name, t in (("k_src", k_src), ("v_src", v_src)):
+            if t.numel() != rows * m["hkv"] * m["d"]:
+                raise ValueError(f"{name} has {t.numel()} elements, expected {rows} x {m['hkv']} x {m['d']}")
+        pool = m["num_pages"] * m["page_size"] * m["hkv"] * m["d"]
+        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.numel() != pool:
+                raise ValueError(f"{name} has {t.numel()} elements, expected {pool}")
+        xattn_write_kv(self._h, k_src.data_ptr(), v_src.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                       stream)
 
     def ready(self) -> bool:
         return xattn_plan_ready(self._h)

@@ -70,6 +70,7 @@ struct Slot {
   // schedule summary and device offsets (in int32 words from dev)
   Schedule sched;
   size_t off_reqs = 0, off_units[xattn::FAM_COUNT] = {0, 0, 0}, off_merges = 0, off_pages = 0;
+  size_t off_kv_start = 0;
   int32_t dtype = 0, hq = 0, hkv = 0, d = 0, page_size = 0, mask = 0, block = 0;
 };
 
@@ -262,6 +263,8 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   words = align_words(words + s.merges.size() * 4);
   const size_t off_pages = words;
   words = align_words(words + s.pages.size());
+  const size_t off_kv_start = words;
+  words = align_words(words + s.kv_start.size());
   const size_t bytes = words * sizeof(int32_t);
 
   int st;
@@ -283,6 +286,7 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
     std::memcpy(img + off_units[f], s.units[f].data(), s.units[f].size() * sizeof(xattn::Unit));
   std::memcpy(img + off_merges, s.merges.data(), s.merges.size() * sizeof(xattn::Merge));
   std::memcpy(img + off_pages, s.pages.data(), s.pages.size() * sizeof(int32_t));
+  std::memcpy(img + off_kv_start, s.kv_start.data(), s.kv_start.size() * sizeof(int32_t));
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   if ((e = hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, strm)) != hipSuccess)
@@ -295,6 +299,7 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   for (int f = 0; f < xattn::FAM_COUNT; ++f) sl.off_units[f] = off_units[f];
   sl.off_merges = off_merges;
   sl.off_pages = off_pages;
+  sl.off_kv_start = off_kv_start;
   sl.dtype = dtype;
   sl.hq = num_qo_heads;
   sl.hkv = num_kv_heads;
@@ -307,6 +312,36 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   h->cur = si;
   return XATTN_OK;
 }
+
+namespace {
+
+// A launch on another stream than the plan's waits for the schedule's copy; on the same
+// stream the copy already precedes it.
+hipError_t slot_wait(Slot& sl, void* stream) {
+  if (stream == sl.plan_stream) return hipSuccess;
+  return hipStreamWaitEvent(static_cast<hipStream_t>(stream), sl.uploaded, 0);
+}
+
+// A launch on another stream than the plan's is not ordered before the slot's next copy
+// by the stream: fence that stream (one event per stream, after its latest launch).
+hipError_t slot_mark(Slot& sl, void* stream) {
+  if (stream == sl.plan_stream) return hipSuccess;
+  size_t i = 0;
+  while (i < sl.foreign_live && sl.foreign[i].first != stream) ++i;
+  if (i == sl.foreign_live) {
+    if (i == sl.foreign.size()) {
+      hipEvent_t ev = nullptr;
+      const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+      sl.foreign.emplace_back(stream, ev);
+    }
+    sl.foreign[i].first = stream;
+    ++sl.foreign_live;
+  }
+  return hipEventRecord(sl.foreign[i].second, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
 
 int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages, void* out,
               float* lse, void* stream) {
@@ -326,11 +361,7 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
 
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e;
-  // a run on another stream than the plan's waits for the schedule's copy; on the same
-  // stream the copy already precedes it
-  if (stream != sl.plan_stream) {
-    if ((e = hipStreamWaitEvent(strm, sl.uploaded, 0)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
-  }
+  if ((e = slot_wait(sl, stream)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
 
   const int32_t* dev = static_cast<const int32_t*>(sl.dev);
   AttnParams p{};
@@ -407,21 +438,57 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
     if ((e = xattn::launch_merge(p, sl.dtype, l)) != hipSuccess) return unused(l), hip_err(e, "merge kernel launch");
     launched(3, l);
   }
-  if (stream != sl.plan_stream) {
-    // not ordered before the slot's next copy by the stream: fence this stream
-    size_t i = 0;
-    while (i < sl.foreign_live && sl.foreign[i].first != stream) ++i;
-    if (i == sl.foreign_live) {
-      if (i == sl.foreign.size()) {
-        hipEvent_t ev = nullptr;
-        if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_err(e, "hipEventCreate");
-        sl.foreign.emplace_back(stream, ev);
-      }
-      sl.foreign[i].first = stream;
-      ++sl.foreign_live;
-    }
-    if ((e = hipEventRecord(sl.foreign[i].second, strm)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  if ((e = slot_mark(sl, stream)) != hipSuccess) return hip_err(e, "hipEventRecord");
+  return XATTN_OK;
+}
+
+int xattn_write_kv(xattn_plan_t plan, const void* k_src, const void* v_src, void* k_pages,
+                   void* v_pages, void* stream) {
+  if (!plan || plan->cur < 0 || !plan->slot[plan->cur].ready)
+    return set_err(XATTN_ERR_INVALID_ARG, "write_kv without a successful plan");
+  Slot& sl = plan->slot[plan->cur];
+  const Schedule& s = sl.sched;
+  if (s.total_kv == 0) return XATTN_OK;
+  if (s.total_kv > INT32_MAX)
+    return set_err(XATTN_ERR_UNSUPPORTED, "contexts of more than 2^31-1 rows in total");
+  if (!k_src || !v_src || !k_pages || !v_pages)
+    return set_err(XATTN_ERR_INVALID_ARG, "k_src, v_src, k_pages and v_pages are required");
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(v_src) |
+                        reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages);
+  if (mis & 15) return set_err(XATTN_ERR_INVALID_ARG, "k_src, v_src, k_pages and v_pages must be 16-byte aligned");
+  const int batch = static_cast<int>(s.reqs.size() / 4);
+  int max_kv = 0;
+  for (int r = 0; r < batch; ++r) max_kv = std::max(max_kv, s.reqs[4 * r + 2]);
+  const int groups = xattn::write_kv_groups(max_kv);
+  if (static_cast<int64_t>(batch) * groups > INT32_MAX)
+    return set_err(XATTN_ERR_UNSUPPORTED, "too many context blocks for one launch");
+
+  hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if ((e = slot_wait(sl, stream)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+  const int32_t* dev = static_cast<const int32_t*>(sl.dev);
+  xattn::WriteParams w{};
+  w.k_src = k_src;
+  w.v_src = v_src;
+  w.k_pages = k_pages;
+  w.v_pages = v_pages;
+  w.reqs = dev + sl.off_reqs;
+  w.kv_start = dev + sl.off_kv_start;
+  w.pages = s.identity ? nullptr : dev + sl.off_pages;
+  w.batch = batch;
+  w.groups = groups;
+  w.page_size = sl.page_size;
+  w.page_shift = -1;
+  if ((sl.page_size & (sl.page_size - 1)) == 0) {
+    int sh = 0;
+    while ((1 << sh) < sl.page_size) ++sh;
+    w.page_shift = sh;
   }
+  w.row_bytes = sl.hkv * sl.d * (sl.dtype == XATTN_BF16 ? 2 : 4);
+  xattn::Launch l;
+  l.stream = strm;
+  if ((e = xattn::launch_write_kv(w, l)) != hipSuccess) return hip_err(e, "context write launch");
+  if ((e = slot_mark(sl, stream)) != hipSuccess) return hip_err(e, "hipEventRecord");
   return XATTN_OK;
 }
 

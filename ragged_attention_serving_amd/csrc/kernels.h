@@ -32,4 +32,22 @@ hipError_t launch_attn_mma(const AttnParams& p, const Launch& l);
 // log-sum-exp merge of split rows into out (dtype 0 fp32, 1 bf16) and lse.
 hipError_t launch_merge(const AttnParams& p, int dtype, const Launch& l);
 
+// Context write: packed per-request rows [sum kv_len][row_bytes] into their page slots.
+struct WriteParams {
+  const void* k_src;
+  const void* v_src;
+  void* k_pages;
+  void* v_pages;
+  const int32_t* reqs;      // [B][4] of the plan (kv_len at 2, page_base at 3)
+  const int32_t* kv_start;  // [B+1] first packed row of each request
+  const int32_t* pages;     // page table, nullptr: identity
+  int32_t batch;
+  int32_t groups;           // blocks per request: write_kv_groups(max kv_len)
+  int32_t page_size;
+  int32_t page_shift;       // log2(page_size) when a power of two, else -1
+  int32_t row_bytes;        // Hkv * head_dim * element size (a multiple of 16)
+};
+int write_kv_groups(int max_kv_len);
+hipError_t launch_write_kv(const WriteParams& w, const Launch& l);
+
 }  // namespace xattn

@@ -124,6 +124,7 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
   if (B > 0 && (a.qo_indptr[0] != 0 || a.kv_indptr[0] != 0))
     return fail(err, kErrInvalid, "qo_indptr[0] and kv_indptr[0] must be 0");
   s.reqs.resize(static_cast<size_t>(B) * 4);
+  s.kv_start.assign(static_cast<size_t>(B) + 1, 0);
   for (int r = 0; r < B; ++r) {
     const int64_t qo = static_cast<int64_t>(a.qo_indptr[r + 1]) - a.qo_indptr[r];
     const int64_t np = static_cast<int64_t>(a.kv_indptr[r + 1]) - a.kv_indptr[r];
@@ -149,6 +150,8 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
     s.reqs[4 * r + 2] = static_cast<int32_t>(kv);
     s.reqs[4 * r + 3] = a.kv_indptr[r];
     s.total_kv += kv;
+    // (context rows past 2^31 are not addressable by the context write; plan still works)
+    s.kv_start[r + 1] = static_cast<int32_t>(std::min<int64_t>(s.total_kv, INT32_MAX));
   }
   s.total_q = B > 0 ? a.qo_indptr[B] : 0;
   if (static_cast<int64_t>(s.total_q) * a.hq > INT32_MAX)

@@ -52,6 +52,7 @@ struct Schedule {
   std::vector<Unit> units[FAM_COUNT];
   std::vector<Merge> merges;
   std::vector<int32_t> pages;  // copy of kv_page_indices (empty: identity table)
+  std::vector<int32_t> kv_start;  // [B+1] cumulative context lengths (packed context rows)
   int64_t ws_rows = 0;
   int32_t dec_rows = 0;
   int32_t tile_rows = kMmaRows;

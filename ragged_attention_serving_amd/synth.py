@@ -39,6 +39,7 @@ MASK_BLOCK_CAUSAL = 2
 
 CHUNK_ELEMS = 1 << 24  # elements per independent child stream
 TENSOR_Q, TENSOR_K, TENSOR_V = 1, 2, 3
+TENSOR_CTX_K, TENSOR_CTX_V = 4, 5  # packed context rows for the context write
 
 
 @dataclass
@@ -216,6 +217,36 @@ def ragged_case(span_lens, num_heads, head_dim, *, num_kv_heads=None, dtype="bf1
                     num_kv_heads=hkv, head_dim=head_dim, page_size=1, mask_mode=mask_mode,
                     block_size=block_size, sm_scale=sm_scale, q=q, k_pages=k, v_pages=v,
                     meta={"cu_seqlens": cu})
+
+
+def ragged_cross_case(q_lens, kv_lens, num_heads, head_dim, *, num_kv_heads=None,
+                      dtype="bf16", seed=0, name="ragged_cross", sm_scale=0.0) -> Workload:
+    """Cacheless cross-attention between two spans of each request: queries packed by
+    cu_q = indptr(q_lens), keys and values by cu_kv = indptr(kv_lens), no mask.
+
+    q is ``[Tq, H, D]``; the pools are k/v ``[Tkv, Hkv, D]`` viewed as ``[Tkv, 1, Hkv, D]``
+    (page_size 1, qo_indptr = cu_q, kv_indptr = cu_kv, no page indices).
+    """
+    hkv = num_heads if num_kv_heads is None else num_kv_heads
+    cu_q, cu_kv = indptr(q_lens), indptr(kv_lens)
+    tq, tkv = int(cu_q[-1]), int(cu_kv[-1])
+    q = normal_tensor((tq, num_heads, head_dim), seed, TENSOR_Q, dtype)
+    k = normal_tensor((tkv, 1, hkv, head_dim), seed, TENSOR_K, dtype)
+    v = normal_tensor((tkv, 1, hkv, head_dim), seed, TENSOR_V, dtype)
+    return Workload(name=name, dtype=dtype, qo_indptr=cu_q, kv_indptr=cu_kv,
+                    kv_page_indices=None, kv_last_page_len=None, num_qo_heads=num_heads,
+                    num_kv_heads=hkv, head_dim=head_dim, page_size=1, mask_mode=MASK_NONE,
+                    block_size=0, sm_scale=sm_scale, q=q, k_pages=k, v_pages=v,
+                    meta={"cu_seqlens": cu_q, "cu_seqlens_kv": cu_kv})
+
+
+def context_source(w: Workload, seed: int = 0):
+    """Packed context keys and values for w's requests: ``[sum kv_len, Hkv, D]`` each, in
+    request order, drawn like the other tensors (N(0,1), rounded to bf16 for bf16)."""
+    rows = int(w.kv_lens().sum())
+    shape = (rows, w.num_kv_heads, w.head_dim)
+    return (normal_tensor(shape, seed, TENSOR_CTX_K, w.dtype),
+            normal_tensor(shape, seed, TENSOR_CTX_V, w.dtype))
 
 
 # ---------------------------------------------------------------- the five workloads

@@ -307,15 +307,61 @@ def pin_brute_force(ref):
 
 
 def pin_cacheless_slices(ref):
-    """Cacheless spans: slicing the packed tensors equals brute force over the spans."""
-    w = synth.ragged_case([5, 9, 1], 4, 8, num_kv_heads=2, dtype="bf16", block_size=4, seed=28)
-    out, lse = ref.ragged_attention(w.q, w.k_pages, w.v_pages, w.meta["cu_seqlens"], 4, 2, dtype="bf16",
-                                    mask_mode=BLOCK, block_size=4)
-    bo, bl = _brute(w)
-    assert np.allclose(out, bo, atol=1e-12, rtol=0) and np.allclose(lse, bl, atol=1e-12, rtol=0)
+    """Cacheless spans: slicing the packed tensors equals brute force over the spans, for
+    self-attention within each span under every mask and for cross-attention between a
+    request's query span and its (differently sized) key span."""
+    cases = [synth.ragged_case([5, 9, 1], 4, 8, num_kv_heads=2, dtype="bf16", block_size=4, seed=28),
+             synth.ragged_case([7, 2, 12], 2, 8, dtype="f32", mask_mode=NONE, seed=29),
+             synth.ragged_case([6, 1, 11], 4, 8, num_kv_heads=1, dtype="bf16", mask_mode=CAUSAL, seed=30),
+             synth.ragged_cross_case([3, 7, 0, 2], [9, 4, 5, 0], 4, 8, num_kv_heads=2, dtype="bf16", seed=31),
+             synth.ragged_cross_case([1, 5], [17, 6], 2, 16, dtype="f32", seed=32)]
+    for w in cases:
+        out, lse = ref.ragged_attention(w.q, w.k_pages, w.v_pages, w.meta["cu_seqlens"], w.num_qo_heads,
+                                        w.num_kv_heads, dtype=w.dtype, mask_mode=w.mask_mode,
+                                        block_size=w.block_size,
+                                        cu_seqlens_kv=w.meta.get("cu_seqlens_kv"))
+        bo, bl = _brute(w)
+        assert np.allclose(out, bo, atol=1e-12, rtol=0), w.name
+        assert np.array_equal(np.isinf(lse), np.isinf(bl)), w.name
+        fin = np.isfinite(bl)
+        assert np.allclose(lse[fin], bl[fin], atol=1e-12, rtol=0), w.name
+
+
+def _write_cases():
+    """Shuffled pages with spare pages and partial last pages, an empty context, page
+    sizes 1, 3 and 4, bf16 and fp32, and the identity table."""
+    return [synth.paged_case([1, 1, 1], [9, 0, 6], 2, 2, 4, 4, dtype="f32", seed=50, extra_pages=3),
+            synth.paged_case([1, 2], [7, 5], 4, 2, 8, 3, dtype="bf16", seed=51, extra_pages=2),
+            synth.ragged_case([3, 5], 2, 4, dtype="f32", mask_mode=NONE, seed=52)]
+
+
+def pin_context_write(ref):
+    """The context write puts position t of request r at slot t % page_size of the page
+    the table lists for t // page_size (walked one position at a time here), bit for bit,
+    and leaves every other slot of both pools as it was."""
+    for w in _write_cases():
+        ks, vs = synth.context_source(w, seed=7)
+        kp, vp = ref.write_context(ks, vs, w.k_pages, w.v_pages, w.kv_indptr, w.kv_page_indices,
+                                   w.kv_last_page_len, w.page_size)
+        written = np.zeros(w.k_pages.shape[:2], bool)
+        row = 0
+        for r in range(w.batch_size):
+            npages = int(w.kv_indptr[r + 1] - w.kv_indptr[r])
+            last = w.page_size if w.kv_last_page_len is None else int(w.kv_last_page_len[r])
+            n = 0 if npages == 0 else (npages - 1) * w.page_size + last
+            for t in range(n):
+                logical = int(w.kv_indptr[r]) + t // w.page_size
+                phys = logical if w.kv_page_indices is None else int(w.kv_page_indices[logical])
+                assert np.array_equal(kp[phys, t % w.page_size], ks[row]), (w.name, r, t)
+                assert np.array_equal(vp[phys, t % w.page_size], vs[row]), (w.name, r, t)
+                written[phys, t % w.page_size] = True
+                row += 1
+        assert row == ks.shape[0]
+        assert np.array_equal(kp[~written], w.k_pages[~written]), w.name
+        assert np.array_equal(vp[~written], w.v_pages[~written]), w.name
 
 
 ALL_PINS = [pin_bf16_widening, pin_lengths, pin_uniform_scores, pin_single_key, pin_two_keys,
             pin_page_permutation, pin_gqa_repeat, pin_key_shift, pin_value_affine,
             pin_request_permutation, pin_split_merge, pin_library_sdpa, pin_brute_force,
-            pin_cacheless_slices]
+            pin_cacheless_slices, pin_context_write]

@@ -119,6 +119,33 @@ def test_single_key_chunks(gpu):
     _full(w, gpu, 1)
 
 
+# ------------------------------------------------------------------ cacheless spans
+
+RAGGED = {
+    # cross-attention between a request's query span and its key span (sizes differ; empty
+    # spans on either side)
+    "ragged_cross_d64": lambda: synth.ragged_cross_case(
+        [3, 70, 1, 130, 0, 9], [1500, 64, 7, 300, 20, 0], 4, 64, seed=40, name="ragged_cross_d64"),
+    "ragged_cross_gqa_d128": lambda: synth.ragged_cross_case(
+        [5, 200, 33], [900, 129, 64], 8, 128, num_kv_heads=2, seed=41, name="ragged_cross_gqa_d128"),
+    "ragged_cross_f32": lambda: synth.ragged_cross_case(
+        [2, 5], [40, 3], 2, 32, dtype="f32", seed=44, name="ragged_cross_f32"),
+    # self-attention within each span without a mask and causally
+    "ragged_self_none_d64": lambda: synth.ragged_case(
+        [200, 17, 65, 1], 4, 64, mask_mode=0, seed=42, name="ragged_self_none_d64"),
+    "ragged_self_causal_d128": lambda: synth.ragged_case(
+        [300, 1, 129], 4, 128, num_kv_heads=2, mask_mode=1, seed=43, name="ragged_self_causal_d128"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RAGGED))
+@pytest.mark.parametrize("chunk", [0, 64, 17])
+def test_cacheless_spans(case, chunk, gpu):
+    """Cacheless spans as the identity page table: cross-attention between two spans of
+    each request, and self-attention within spans with no mask or a causal one."""
+    _full(RAGGED[case](), gpu, chunk)
+
+
 def test_empty_batch(gpu):
     import ragged_attention_serving_amd as xa
     import torch

@@ -10,7 +10,7 @@ import oracle.ref as ref
 from tests import oracle_pins
 
 _orig = {n: getattr(ref, n) for n in ("to_f64", "request_lengths", "gather_pages", "visible",
-                                      "attend", "merge_states")}
+                                      "attend", "merge_states", "ragged_attention", "write_context")}
 
 
 def _gather_reversed_pages(pool, kv_indptr, kv_page_indices, r, kv_len, page_size, kv_head):
@@ -104,7 +104,47 @@ def _merge_no_weights(outs, lses):
     return outs.mean(0), M
 
 
+def _ragged_keys_from_query_spans(*args, **kw):
+    kw.pop("cu_seqlens_kv", None)
+    return _orig["ragged_attention"](*args, **kw)
+
+
+def _write_slot_from_page_index(k_src, v_src, k_pages, v_pages, kv_indptr, kv_page_indices,
+                                kv_last_page_len, page_size):
+    kp, vp = np.array(k_pages, copy=True), np.array(v_pages, copy=True)
+    _, kv_len = ref.request_lengths(np.zeros(len(kv_indptr), np.int64), kv_indptr, kv_last_page_len,
+                                    page_size)
+    start = 0
+    for r in range(len(kv_indptr) - 1):
+        for t in range(int(kv_len[r])):
+            logical = int(kv_indptr[r]) + t // page_size
+            page = logical if kv_page_indices is None else int(kv_page_indices[logical])
+            kp[page, (t // page_size) % page_size] = k_src[start + t]
+            vp[page, (t // page_size) % page_size] = v_src[start + t]
+        start += int(kv_len[r])
+    return kp, vp
+
+
+def _write_ignores_table(k_src, v_src, k_pages, v_pages, kv_indptr, kv_page_indices,
+                         kv_last_page_len, page_size):
+    return _orig["write_context"](k_src, v_src, k_pages, v_pages, kv_indptr, None, kv_last_page_len,
+                                  page_size)
+
+
+def _write_clears_tails(k_src, v_src, k_pages, v_pages, kv_indptr, kv_page_indices,
+                        kv_last_page_len, page_size):
+    kp, vp = _orig["write_context"](k_src, v_src, k_pages, v_pages, kv_indptr, kv_page_indices,
+                                    kv_last_page_len, page_size)
+    kp[:, -1] = 0
+    vp[:, -1] = 0
+    return kp, vp
+
+
 MUTATIONS = {
+    "write_slot_from_page_index": ("write_context", _write_slot_from_page_index),
+    "write_ignores_table": ("write_context", _write_ignores_table),
+    "write_clears_tails": ("write_context", _write_clears_tails),
+    "ragged_keys_from_query_spans": ("ragged_attention", _ragged_keys_from_query_spans),
     "gather_reversed_pages": ("gather_pages", _gather_reversed_pages),
     "gather_ignores_table": ("gather_pages", _gather_ignores_table),
     "gather_wrong_head": ("gather_pages", _gather_wrong_head),

@@ -317,6 +317,17 @@ def main():
             log(f"[bench] {json.dumps(r)}")
             del ws, ms
             torch.cuda.empty_cache()
+        for name, fn in synth.TP_WORKLOADS.items():
+            log(f"[bench] sweep: generating {name}")
+            ws = fn(0)
+            log(f"[bench] sweep: measuring {name}")
+            ms = measure(ws, max(5, min(args.steps, 20)), 3, dev)
+            r = summarize(ws, ms)
+            r.pop("schedule", None)
+            sweep[name] = r
+            log(f"[bench] {json.dumps(r)}")
+            del ws, ms
+            torch.cuda.empty_cache()
         log("[bench] sweep: context write")
         wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), max(5, min(args.steps, 20)), 3, dev)
         sweep[wr["workload"]] = wr

@@ -291,10 +291,34 @@ def gqa_decode(seed: int = 0) -> Workload:
                       seed=seed, rng=rng, name="gqa_decode_causal")
 
 
+def gqa_decode_tp8(seed: int = 0) -> Workload:
+    """One rank's share of the GQA decode under tensor parallelism over heads, degree 8
+    (page "mstar.model.components.distributed.attention", ParallelAttention: each rank
+    holds num_heads / tp query heads and num_kv_heads / tp KV heads): 4 q heads and 1 KV
+    head per rank, the same 256 contexts and pages."""
+    rng = np.random.default_rng(seed)
+    kv = np.rint(np.exp(rng.uniform(math.log(512), math.log(32768), 256))).astype(np.int64)
+    return paged_case([1] * 256, kv, 4, 1, 128, 16, dtype="bf16", mask_mode=MASK_CAUSAL,
+                      seed=seed, rng=rng, name="gqa_decode_causal_tp8")
+
+
+def whisper_decode_tp4(seed: int = 0) -> Workload:
+    """One rank's share of the Whisper-style decode at tensor parallelism 4: 5 of the 20
+    heads (query and KV alike), the same 64 contexts of 1500 positions."""
+    return paged_case([1] * 64, [1500] * 64, 5, 5, 64, 16, dtype="bf16", seed=seed,
+                      name="whisper_decode_cross_tp4", sm_scale=1.0 / 8.0)
+
+
 WORKLOADS = {
     "tiny_cross_f32": tiny_cross,
     "whisper_decode_cross": whisper_decode,
     "ragged_prefill_cross": ragged_prefill,
     "block_causal_ragged": block_causal,
     "gqa_decode_causal": gqa_decode,
+}
+
+# per-rank shapes of tensor parallelism over heads, measured on one GPU
+TP_WORKLOADS = {
+    "gqa_decode_causal_tp8": gqa_decode_tp8,
+    "whisper_decode_cross_tp4": whisper_decode_tp4,
 }

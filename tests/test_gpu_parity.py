@@ -53,6 +53,19 @@ def test_block_causal_sampled(gpu):
     assert np.isfinite(lse).all() and not np.isnan(out).any()
 
 
+def test_tensor_parallel_rank_shapes(gpu):
+    """One rank's heads of the decode workloads under tensor parallelism over heads."""
+    w = synth.whisper_decode_tp4(0)
+    _full(w, gpu)
+    w = synth.gqa_decode_tp8(0)
+    log(f"[parity] {w.name} (sampled requests)")
+    out, lse, plan = run_gpu(w, gpu)
+    kv = w.kv_lens()
+    reqs = sorted({int(np.argmax(kv)), int(np.argmin(kv)), 0, 77, 255})
+    ro, rl = ref.run_workload(w, requests=reqs)
+    compare(out[reqs], lse[reqs], ro[reqs], rl[reqs], w.dtype, label=f"{w.name} requests {reqs}")
+
+
 def test_gqa_decode_sampled(gpu):
     w = synth.gqa_decode(0)
     log(f"[parity] {w.name} (sampled requests)")

@@ -141,6 +141,14 @@ XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int
  * the schedule's copy and records an event that the next plan into this slot waits
  * for; a run on the plan's stream records nothing. Streams used by runs must stay
  * valid until the handle's next-but-one xattn_plan or its destruction.
+ *
+ * Graph capture (page "mstar.engine.resources.attn.cross", force_double_buffer: the plan
+ * keeps two buffers so that a captured graph can read one while the next plan fills the
+ * other). A run on the plan's own stream with timing off issues kernel launches only, so
+ * it may be captured into a HIP graph. A replay repeats the captured schedule with the
+ * captured pointers: it stays valid through the handle's next xattn_plan (which fills
+ * the other slot) and must not be replayed after the one after that, which reuses (and
+ * may reallocate) the slot it reads.
  */
 XATTN_API int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
               void* out, float* lse, void* stream);

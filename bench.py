@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "mfma": "ragged_attention_serving_amd/csrc/attn_mma.hip",
     "fp32": "ragged_attention_serving_amd/csrc/attn_f32.hip",
     "merge": "ragged_attention_serving_amd/csrc/merge.hip",
+    "write": "ragged_attention_serving_amd/csrc/write_kv.hip",
 }
 TIMING_EVERY = 5  # kernel start/end events on every 5th timed run
 KERNEL_NAMES = {"decode": "attn_decode_kernel", "mfma": "attn_mma_kernel", "fp32": "attn_f32_kernel",
@@ -242,6 +243,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device once (the known-size kernel that scales "
                          "the FETCH_SIZE and WRITE_SIZE counters) and exit")
+    ap.add_argument("--context-write", action="store_true",
+                    help="only time the context write (xattn_write_kv) of the workload's contexts "
+                         "and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -260,8 +264,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 4}), flush=True)
         return
+    all_workloads = {**synth.WORKLOADS, **synth.TP_WORKLOADS}
     log(f"[bench] generating {args.workload}")
-    w = synth.WORKLOADS[args.workload](0)
+    w = all_workloads[args.workload](0)
+    if args.context_write:
+        print(json.dumps(measure_write(w, args.steps, args.warmup, dev)), flush=True)
+        return
     log(f"[bench] measuring {args.workload}: steps={args.steps} warmup={args.warmup}")
     m = measure(w, args.steps, args.warmup, dev, args.cold_steps)
     res = summarize(w, m)

@@ -1,0 +1,97 @@
+"""GPU parity at the size limits and for the call errors of the C ABI.
+
+- Contexts far past the per-unit page caps (split by the partitioner and merged), for the
+  decode and the tile kernels, paged and identity tables.
+- Many requests, wide head groups, and the largest decode row count.
+- Argument errors that the library must report without launching anything.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from ragged_attention_serving_amd import synth
+from tests.gpu_util import compare, log, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, gpu, reqs=None, chunk=0):
+    log(f"[limits] {w.name}")
+    out, lse, plan = run_gpu(w, gpu, chunk)
+    log(f"  schedule {plan.info()}")
+    if reqs is None:
+        ro, rl = ref.run_workload(w)
+        compare(out, lse, ro, rl, w.dtype, label=w.name)
+    else:
+        ro, rl = ref.run_workload(w, requests=reqs)
+        rows = np.concatenate([np.arange(w.qo_indptr[r], w.qo_indptr[r + 1]) for r in reqs])
+        compare(out, lse, ro, rl, w.dtype, rows=rows, label=f"{w.name} requests {reqs}")
+    plan.close()
+
+
+def test_decode_context_past_the_page_cap(gpu):
+    # 100k keys at page_size 16 is 6250 pages, three times the decode unit's page cap
+    w = synth.paged_case([1, 1], [100000, 37], 8, 2, 128, 16, mask_mode=1, seed=80, name="decode_100k")
+    _check(w, gpu)
+
+
+def test_prefill_context_past_the_page_cap(gpu):
+    # tile units hold at most 1022 pages: 40k keys at page_size 16 is 2500 pages
+    w = synth.paged_case([200, 3], [40000, 9], 4, 4, 64, 16, seed=81, name="prefill_40k")
+    _check(w, gpu)
+
+
+def test_long_cacheless_span(gpu):
+    w = synth.ragged_case([9000, 70], 2, 128, block_size=64, seed=82, name="block_causal_9000")
+    _check(w, gpu, reqs=[0, 1])
+
+
+def test_many_short_requests(gpu):
+    rng = np.random.default_rng(83)
+    kv = rng.integers(1, 200, 3000)
+    w = synth.paged_case([1] * 3000, kv, 4, 4, 64, 16, seed=83, name="decode_3000_requests")
+    _check(w, gpu, reqs=[0, 1, 1500, 2999])
+
+
+def test_wide_head_groups(gpu):
+    # 16 query heads per KV head: a decode token already has 16 rows (tile kernel); 2 tokens of
+    # 4 heads per KV head are the decode kernel's largest unit (8 rows)
+    w = synth.paged_case([1, 2, 7], [3000, 500, 900], 32, 2, 128, 16, mask_mode=1, seed=84, name="gqa16")
+    _check(w, gpu)
+    w = synth.paged_case([2, 2, 1], [3000, 5, 900], 8, 2, 64, 16, mask_mode=1, seed=85, name="decode_rows8")
+    _check(w, gpu)
+
+
+def test_argument_errors_are_reported(gpu):
+    import torch
+    import ragged_attention_serving_amd as xa
+    w = synth.paged_case([1, 3], [40, 20], 2, 2, 64, 16, seed=86)
+    q, k, v = (to_device(x, "bf16", gpu) for x in (w.q, w.k_pages, w.v_pages))
+    out = torch.empty_like(q)
+    plan = xa.Plan()
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, 2, 2, 64, 16, w.num_pages)
+    h = plan.handle
+    L = xa.lib()
+    # misaligned q, missing out, misaligned lse: rejected before any launch
+    assert L.xattn_run(h, q.data_ptr() + 2, k.data_ptr(), v.data_ptr(), out.data_ptr(), None, None) == xa.XATTN_ERR_INVALID_ARG
+    assert "aligned" in xa.xattn_last_error()
+    assert L.xattn_run(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), None, None, None) == xa.XATTN_ERR_INVALID_ARG
+    lse = torch.empty(8, dtype=torch.float32, device=gpu)
+    assert L.xattn_run(h, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       ctypes.c_void_p(lse.data_ptr() + 2), None) == xa.XATTN_ERR_INVALID_ARG
+    # the context write needs all four pointers, 16-byte aligned
+    assert L.xattn_write_kv(h, None, v.data_ptr(), k.data_ptr(), v.data_ptr(), None) == xa.XATTN_ERR_INVALID_ARG
+    assert L.xattn_write_kv(h, k.data_ptr() + 8, v.data_ptr(), k.data_ptr(), v.data_ptr(), None) == xa.XATTN_ERR_INVALID_ARG
+    # a failed plan keeps the previous schedule: the run still matches the oracle
+    bad = np.array(w.kv_page_indices)
+    bad[0] = w.num_pages + 5
+    with pytest.raises(xa.XattnError):
+        plan.plan(w.qo_indptr, w.kv_indptr, bad, w.kv_last_page_len, 2, 2, 64, 16, w.num_pages)
+    o, l = plan.run(q, k, v)
+    torch.cuda.synchronize()
+    from tests.gpu_util import from_device
+    ro, rl = ref.run_workload(w)
+    compare(from_device(o), l.cpu().numpy().astype(np.float64), ro, rl, "bf16", label="after a failed plan")
+    plan.close()

@@ -196,36 +196,56 @@ def traffic_for(stage: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The fp64 oracle as it stands, on this host, over whole passes of the workload."""
+_CPU_W = None  # the workload, shared with forked workers
+
+
+def _cpu_worker(args):
+    """One process: oracle passes over requests start, start+step, ... for wall_s seconds."""
+    start, step, wall_s = args
     try:
         from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(1)  # one BLAS thread per process
     except Exception:  # pragma: no cover
-        threadpool_limits = None
+        ctx = None
     from oracle import ref
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    if ctx:
-        ctx.__enter__()
-    try:
-        kv_bytes = int(w.kv_lens().sum()) * w.num_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
-        reqs = list(range(w.batch_size))
-        done_bytes = 0
-        done_req = 0
+    w = _CPU_W
+    elt = 2 if w.dtype == "bf16" else 4
+    kv = w.kv_lens()
+    done_bytes, done_req, i = 0, 0, start
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < wall_s:
+        r = i % w.batch_size
+        ref.run_workload(w, requests=[r])
+        done_bytes += int(kv[r]) * w.num_kv_heads * w.head_dim * 2 * elt
+        done_req += 1
+        i += step
+    el = time.perf_counter() - t0
+    del ctx  # (the limit only needs to hold while this worker runs)
+    return done_bytes, done_req, el
+
+
+def cpu_baseline(w, cpu_seconds=24.0):
+    """The fp64 oracle as it stands, on this host's cores: one process per core (at most 16),
+    each taking whole requests (all heads) in turn for cpu_seconds / processes (at least 2 s)
+    of wall time.
+    Must run before the process touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    global _CPU_W
+    _CPU_W = w
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    wall = max(2.0, cpu_seconds / n)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(n) as pool:
         t0 = time.perf_counter()
-        i = 0
-        while time.perf_counter() - t0 < budget_s:
-            r = reqs[i % len(reqs)]
-            ref.run_workload(w, requests=[r])
-            done_bytes += int(w.kv_lens()[r]) * w.num_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
-            done_req += 1
-            i += 1
+        parts = pool.map(_cpu_worker, [(k, n, wall) for k in range(n)])
         el = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_req} request passes (all {w.num_qo_heads} heads each, {done_req / len(reqs):.2f} "
-                      f"x the workload's {len(reqs)} requests) in {el:.1f} s, one thread",
+    done_bytes = sum(p[0] for p in parts)
+    done_req = sum(p[1] for p in parts)
+    elt = 2 if w.dtype == "bf16" else 4
+    kv_bytes = int(w.kv_lens().sum()) * w.num_kv_heads * w.head_dim * 2 * elt
+    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+            "sample": f"{done_req} request passes (all {w.num_qo_heads} heads each, {done_req / w.batch_size:.2f} "
+                      f"x the workload's {w.batch_size} requests) by {n} processes in {el:.1f} s",
             "workload_bytes": kv_bytes}
 
 
@@ -237,7 +257,8 @@ def main():
     ap.add_argument("--workload", default="whisper_decode_cross")
     ap.add_argument("--all", action="store_true", help="also measure every other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="CPU seconds (summed over the worker processes) for the oracle baseline")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="runs timed one by one after a 1 GiB cache flush (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -254,6 +275,13 @@ def main():
 
     import torch
     from ragged_attention_serving_amd import synth
+
+    cpu_line = None
+    if not (args.no_cpu_baseline or args.copy_calibration or args.context_write):
+        # before anything touches the GPU: the oracle's worker processes are forked
+        log(f"[bench] timing the CPU oracle on {args.workload}")
+        cpu_line = cpu_baseline({**synth.WORKLOADS, **synth.TP_WORKLOADS}[args.workload](0), args.cpu_seconds)
+        log(f"[bench] cpu baseline {json.dumps(cpu_line)}")
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -307,9 +335,8 @@ def main():
         "plan_ms": res["plan_ms"],
         "schedule": res["schedule"],
     }
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if cpu_line is not None:
+        line["cpu_baseline"] = cpu_line
     if args.all:
         sweep = {}
         for name, fn in synth.WORKLOADS.items():

@@ -25,7 +25,7 @@ def test_tiny_cross_golden():
 
 
 def test_generator_self_check():
-    """Lengths of the seeded workloads (the survey's self-check values)."""
+    """Lengths of the seeded workloads: numpy 2.2 draws from default_rng(0) in the fixed order."""
     w3 = synth.ragged_prefill(0)
     assert int(w3.qo_indptr[-1]) == 7569 and list(w3.qo_lens()[:4]) == [382, 286, 229, 121]
     assert w3.k_pages.shape == (3008, 16, 20, 64)

@@ -115,6 +115,29 @@ enum xattn_status {
  *
  * On error the handle (if any) keeps its previous schedule unchanged.
  */
+enum xattn_plan_flags {
+  XATTN_PLAN_GRAPH_STABLE = 1
+};
+
+/*
+ * xattn_plan_create: an empty handle with flags (xattn_plan creates one with no flags
+ * when *plan is NULL). *plan must be NULL on entry.
+ *
+ * XATTN_PLAN_GRAPH_STABLE (page "mstar.engine.resources.attn.cross",
+ * force_double_buffer: the plan keeps two buffers so that a captured graph reads one
+ * while the next plan fills the other). Each slot lays its device schedule out by
+ * capacities that only grow (with a quarter of headroom when they do), and a run
+ * launches every kernel family the slot has held, with grids of the slot's capacity;
+ * blocks past the current plan's units exit at once. A run captured into a HIP graph
+ * (on the plan's stream, timing off) then replays correctly for any later schedule in
+ * the same slot as long as the slot's layout_generation (xattn_plan_info) is unchanged;
+ * when it changes, capture again. Keep one graph per slot: consecutive plans alternate
+ * slots (xattn_plan_info's `slot`). The q, k_pages, v_pages, out and lse pointers are
+ * part of the capture. Costs a few idle blocks per launch; without the flag, grids
+ * match each schedule exactly.
+ */
+XATTN_API int xattn_plan_create(xattn_plan_t* plan, int32_t flags);
+
 XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
                const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
                int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
@@ -198,6 +221,10 @@ typedef struct xattn_schedule_info {
   int64_t workspace_rows;   /* fp32 partial rows (head_dim values + 1 lse each) */
   int64_t total_kv_tokens;  /* sum over requests of kv_len */
   int64_t visible_pairs;    /* sum over query rows and heads of visible keys */
+  int64_t layout_generation; /* xattn_plan_info: the slot's layout generation (see
+                                XATTN_PLAN_GRAPH_STABLE); 0 from xattn_schedule */
+  int32_t slot;             /* xattn_plan_info: the slot (0 or 1) the schedule is in */
+  int32_t reserved;
 } xattn_schedule_info;
 
 /*

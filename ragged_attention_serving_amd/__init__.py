@@ -32,7 +32,7 @@ XATTN_ERR_OOM = -4
 XATTN_ERR_BUSY = -5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
-EXPORTED = ("xattn_plan", "xattn_run", "xattn_write_kv", "xattn_plan_ready", "xattn_plan_destroy",
+EXPORTED = ("xattn_plan_create", "xattn_plan", "xattn_run", "xattn_write_kv", "xattn_plan_ready", "xattn_plan_destroy",
             "xattn_last_error", "xattn_schedule", "xattn_plan_info", "xattn_plan_set_timing",
             "xattn_plan_timing")
 STAGES = ("fp32", "decode", "mfma", "merge")
@@ -50,13 +50,15 @@ class ScheduleInfo(ctypes.Structure):
     _fields_ = [("num_units", ctypes.c_int32 * 3), ("chunk_tokens", ctypes.c_int32 * 3),
                 ("decode_rows", ctypes.c_int32), ("num_merge_rows", ctypes.c_int32),
                 ("workspace_rows", ctypes.c_int64), ("total_kv_tokens", ctypes.c_int64),
-                ("visible_pairs", ctypes.c_int64)]
+                ("visible_pairs", ctypes.c_int64), ("layout_generation", ctypes.c_int64),
+                ("slot", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {"num_units": list(self.num_units), "chunk_tokens": list(self.chunk_tokens),
                 "decode_rows": self.decode_rows, "num_merge_rows": self.num_merge_rows,
                 "workspace_rows": self.workspace_rows, "total_kv_tokens": self.total_kv_tokens,
-                "visible_pairs": self.visible_pairs}
+                "visible_pairs": self.visible_pairs, "layout_generation": self.layout_generation,
+                "slot": self.slot}
 
 
 def lib() -> ctypes.CDLL:
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.xattn_plan.argtypes = [ctypes.POINTER(vp), P32, P32, P32, P32, i32, i32, i32, i32, i32, i64,
                              i32, i32, f32, i32, vp]
     L.xattn_plan.restype = ctypes.c_int
+    L.xattn_plan_create.argtypes = [ctypes.POINTER(vp), i32]
+    L.xattn_plan_create.restype = ctypes.c_int
     L.xattn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.xattn_run.restype = ctypes.c_int
     L.xattn_write_kv.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -191,6 +195,14 @@ def xattn_run(handle, q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, lse_ptr:
     _check(lib().xattn_run(handle, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr or None, _stream_handle(stream)))
 
 
+PLAN_GRAPH_STABLE = 1
+
+
+def xattn_plan_create(handle, flags: int = 0) -> None:
+    """Creates an empty handle in `handle` (a ctypes.c_void_p holding NULL) with flags."""
+    _check(lib().xattn_plan_create(ctypes.byref(handle), flags))
+
+
 def xattn_write_kv(handle, k_src_ptr: int, v_src_ptr: int, k_pages_ptr: int, v_pages_ptr: int,
                    stream=None) -> None:
     """Raw context write on device pointers (ints)."""
@@ -232,10 +244,14 @@ def xattn_plan_destroy(handle) -> None:
 class Plan:
     """One attention handle: plan once per step, run once per layer."""
 
-    def __init__(self):
+    def __init__(self, graph_stable: bool = False):
+        """graph_stable: lay each slot out for HIP-graph replay across plans
+        (XATTN_PLAN_GRAPH_STABLE; see xattn_plan_create)."""
         lib()
         self._h = ctypes.c_void_p()
         self.meta = None
+        if graph_stable:
+            xattn_plan_create(self._h, PLAN_GRAPH_STABLE)
 
     def plan(self, qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, num_qo_heads,
              num_kv_heads, head_dim, page_size, num_pages, mask_mode=MASK_NONE, block_size=0,

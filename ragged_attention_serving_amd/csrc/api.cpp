@@ -71,6 +71,16 @@ struct Slot {
   Schedule sched;
   size_t off_reqs = 0, off_units[xattn::FAM_COUNT] = {0, 0, 0}, off_merges = 0, off_pages = 0;
   size_t off_kv_start = 0;
+  // graph-stable layout: section capacities (elements) that only grow, what every run
+  // launches (the union over plans), and the generation of the layout
+  size_t cap_reqs = 0, cap_units[xattn::FAM_COUNT] = {0, 0, 0}, cap_merges = 0, cap_pages = 0,
+         cap_kv_start = 0;
+  int64_t cap_ws_rows = 0;
+  int run_fams = 0;       // bit f: family f is launched
+  bool run_merge = false;
+  int run_dec_rows = 0;
+  std::vector<int64_t> layout_key;
+  int64_t layout_gen = 0;
   int32_t dtype = 0, hq = 0, hkv = 0, d = 0, page_size = 0, mask = 0, block = 0;
 };
 
@@ -83,6 +93,7 @@ struct TimingRec {
 
 struct xattn_plan_s {
   Slot slot[2];
+  int flags = 0;  // XATTN_PLAN_GRAPH_STABLE
   int cur = -1;
   int device = 0;
   int timing_every = 0;  // record kernel events on every n-th run (0: off)
@@ -132,6 +143,9 @@ void fill_info(const Schedule& s, xattn_schedule_info* info) {
   info->workspace_rows = s.ws_rows;
   info->total_kv_tokens = s.total_kv;
   info->visible_pairs = s.visible_pairs;
+  info->layout_generation = 0;
+  info->slot = -1;
+  info->reserved = 0;
 }
 
 xattn::PlanArgs make_args(const int32_t* qo_indptr, const int32_t* kv_indptr,
@@ -250,27 +264,41 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   }
   sl.foreign_live = 0;
 
-  // device image: reqs | units per family | merges | page indices (int32 words)
+  // device image (int32 words): header | reqs | units per family | merges | page indices |
+  // kv starts. The header holds each family's unit count and the merge count, which the
+  // kernels read in a graph-stable handle. There the sections are laid out by capacities
+  // that only grow (a quarter of headroom when they do), so offsets and buffers stay put
+  // from plan to plan while the schedule fits, and the workspace likewise.
+  const bool stable = (h->flags & XATTN_PLAN_GRAPH_STABLE) != 0;
+  auto fit = [&](size_t& cap, size_t need) {
+    if (!stable) cap = need;
+    else if (need > cap) cap = need + need / 4;
+    return cap;
+  };
   size_t words = 0;
+  constexpr size_t kHeaderWords = 64;
+  words += kHeaderWords;
   const size_t off_reqs = words;
-  words = align_words(words + s.reqs.size());
+  words = align_words(words + fit(sl.cap_reqs, s.reqs.size()));
   size_t off_units[xattn::FAM_COUNT];
   for (int f = 0; f < xattn::FAM_COUNT; ++f) {
     off_units[f] = words;
-    words = align_words(words + s.units[f].size() * 8);
+    words = align_words(words + fit(sl.cap_units[f], s.units[f].size()) * 8);
   }
   const size_t off_merges = words;
-  words = align_words(words + s.merges.size() * 4);
+  words = align_words(words + fit(sl.cap_merges, s.merges.size()) * 4);
   const size_t off_pages = words;
-  words = align_words(words + s.pages.size());
+  words = align_words(words + fit(sl.cap_pages, s.pages.size()));
   const size_t off_kv_start = words;
-  words = align_words(words + s.kv_start.size());
+  words = align_words(words + fit(sl.cap_kv_start, s.kv_start.size()));
   const size_t bytes = words * sizeof(int32_t);
+  if (!stable) sl.cap_ws_rows = s.ws_rows;
+  else if (s.ws_rows > sl.cap_ws_rows) sl.cap_ws_rows = s.ws_rows + s.ws_rows / 4;
 
   int st;
   if ((st = ensure(&sl.host, &sl.host_cap, bytes, true)) != XATTN_OK) return fail(st);
   if ((st = ensure(&sl.dev, &sl.dev_cap, bytes, false)) != XATTN_OK) return fail(st);
-  const size_t ws_bytes = static_cast<size_t>(s.ws_rows) * (head_dim + 1) * sizeof(float);
+  const size_t ws_bytes = static_cast<size_t>(sl.cap_ws_rows) * (head_dim + 1) * sizeof(float);
   if (ws_bytes > 0) {
     void* w = sl.ws;
     if ((st = ensure(&w, &sl.ws_cap, ws_bytes, false)) != XATTN_OK) {
@@ -281,6 +309,9 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   }
 
   int32_t* img = static_cast<int32_t*>(sl.host);
+  std::memset(img, 0, kHeaderWords * sizeof(int32_t));
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) img[f] = static_cast<int32_t>(s.units[f].size());
+  img[3] = static_cast<int32_t>(s.merges.size());
   std::memcpy(img + off_reqs, s.reqs.data(), s.reqs.size() * sizeof(int32_t));
   for (int f = 0; f < xattn::FAM_COUNT; ++f)
     std::memcpy(img + off_units[f], s.units[f].data(), s.units[f].size() * sizeof(xattn::Unit));
@@ -307,9 +338,47 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   sl.page_size = page_size;
   sl.mask = mask_mode;
   sl.block = block_size;
+  // what a run launches: this schedule's kernels, or in a graph-stable handle the union
+  // over the slot's plans (a launch whose count is 0 this time exits at once)
+  int fams = 0;
+  for (int f = 0; f < xattn::FAM_COUNT; ++f)
+    if (!s.units[f].empty()) fams |= 1 << f;
+  sl.run_fams = stable ? (sl.run_fams | fams) : fams;
+  sl.run_merge = stable ? (sl.run_merge || !s.merges.empty()) : !s.merges.empty();
+  sl.run_dec_rows = stable ? std::max(sl.run_dec_rows, s.dec_rows) : s.dec_rows;
+  // everything a captured run holds as a launch argument or launch shape; any change
+  // starts a new layout generation
+  std::vector<int64_t> key = {
+      reinterpret_cast<int64_t>(sl.dev), reinterpret_cast<int64_t>(sl.ws), sl.cap_ws_rows,
+      static_cast<int64_t>(off_reqs), static_cast<int64_t>(off_merges), static_cast<int64_t>(off_pages),
+      static_cast<int64_t>(off_kv_start), static_cast<int64_t>(sl.cap_merges), sl.run_fams,
+      sl.run_merge, sl.run_dec_rows, s.identity, s.group, s.tile_rows, dtype, num_qo_heads,
+      num_kv_heads, head_dim, page_size, mask_mode, block_size};
+  for (int f = 0; f < xattn::FAM_COUNT; ++f) {
+    key.push_back(static_cast<int64_t>(off_units[f]));
+    key.push_back(static_cast<int64_t>(sl.cap_units[f]));
+  }
+  int32_t scale_bits;
+  std::memcpy(&scale_bits, &s.scale, sizeof(scale_bits));
+  key.push_back(scale_bits);
+  if (key != sl.layout_key) {
+    sl.layout_key = std::move(key);
+    ++sl.layout_gen;
+  }
   sl.sched = std::move(s);
   sl.ready = true;
   h->cur = si;
+  return XATTN_OK;
+}
+
+int xattn_plan_create(xattn_plan_t* plan, int32_t flags) {
+  if (!plan) return set_err(XATTN_ERR_INVALID_ARG, "plan is NULL");
+  if (*plan) return set_err(XATTN_ERR_INVALID_ARG, "*plan is not NULL");
+  if (flags & ~XATTN_PLAN_GRAPH_STABLE) return set_err(XATTN_ERR_INVALID_ARG, "unknown flags");
+  xattn_plan_s* h = new xattn_plan_s();
+  h->flags = flags;
+  (void)hipGetDevice(&h->device);
+  *plan = h;
   return XATTN_OK;
 }
 
@@ -370,8 +439,9 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   p.v = v_pages;
   p.out = out;
   p.lse = lse;
+  const bool stable = (plan->flags & XATTN_PLAN_GRAPH_STABLE) != 0;
   p.ws_o = sl.ws;
-  p.ws_lse = sl.ws ? sl.ws + static_cast<size_t>(s.ws_rows) * sl.d : nullptr;
+  p.ws_lse = sl.ws ? sl.ws + static_cast<size_t>(sl.cap_ws_rows) * sl.d : nullptr;
   p.reqs = dev + sl.off_reqs;
   p.pages = s.identity ? nullptr : dev + sl.off_pages;
   p.merges = dev + sl.off_merges;
@@ -420,19 +490,27 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
     if (l.stop) plan->event_pool.push_back(l.stop);
   };
 
+  // a graph-stable handle launches every family the slot has seen with grids of the
+  // slot's capacity; the kernels read the real counts from the image header
   for (int f = 0; f < xattn::FAM_COUNT; ++f) {
-    if (s.units[f].empty()) continue;
+    if (stable ? !(sl.run_fams & (1 << f)) : s.units[f].empty()) continue;
     p.units = dev + sl.off_units[f];
-    p.num_units = static_cast<int32_t>(s.units[f].size());
+    p.num_units = static_cast<int32_t>(stable ? sl.cap_units[f] : s.units[f].size());
+    p.unit_count = stable ? dev + f : nullptr;
+    if (p.num_units == 0) continue;
     xattn::Launch l;
     if ((e = launch_for(l)) != hipSuccess) return unused(l), hip_err(e, "timing event");
     if (f == xattn::FAM_F32) e = xattn::launch_attn_f32(p, l);
-    else if (f == xattn::FAM_DEC) e = xattn::launch_attn_decode(p, s.dec_rows, l);
+    else if (f == xattn::FAM_DEC) e = xattn::launch_attn_decode(p, stable ? sl.run_dec_rows : s.dec_rows, l);
     else e = xattn::launch_attn_mma(p, l);
     if (e != hipSuccess) return unused(l), hip_err(e, "attention kernel launch");
     launched(f, l);
   }
-  if (!s.merges.empty()) {
+  if (stable) {
+    p.num_merges = sl.run_merge ? static_cast<int32_t>(sl.cap_merges) : 0;
+    p.merge_count = dev + 3;
+  }
+  if (p.num_merges > 0) {
     xattn::Launch l;
     if ((e = launch_for(l)) != hipSuccess) return unused(l), hip_err(e, "timing event");
     if ((e = xattn::launch_merge(p, sl.dtype, l)) != hipSuccess) return unused(l), hip_err(e, "merge kernel launch");
@@ -512,6 +590,8 @@ int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info) {
   if (!plan || !info) return set_err(XATTN_ERR_INVALID_ARG, "NULL argument");
   if (plan->cur < 0) return set_err(XATTN_ERR_INVALID_ARG, "no schedule yet");
   fill_info(plan->slot[plan->cur].sched, info);
+  info->layout_generation = plan->slot[plan->cur].layout_gen;
+  info->slot = plan->cur;
   return XATTN_OK;
 }
 

@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p) {
   __shared__ float sS[kRows][kMaxChunk];
   __shared__ float sM[kRows], sL[kRows];
 
+  if (p.unit_count && static_cast<int>(blockIdx.x) >= *p.unit_count) return;  // past this plan's units
   const int* u = p.units + static_cast<int64_t>(blockIdx.x) * 8;
   const int r = u[0], hk = u[1], row0 = u[2], nrows = u[3], kv0 = u[4], kv1 = u[5], ws_row = u[6];
   const int* rq = p.reqs + 4 * r;

@@ -83,6 +83,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   __shared__ __attribute__((aligned(1024))) char sk0[C::TILE], sk1[C::TILE];
   __shared__ __attribute__((aligned(1024))) char sv0[C::TILE], sv1[C::TILE];
 
+  if (p.unit_count && static_cast<int>(blockIdx.x) >= *p.unit_count) return;  // past this plan's units
   const int* u = p.units + static_cast<int64_t>(blockIdx.x) * 8;
   const int r = u[0], hk = u[1], row0 = u[2], nrows = u[3], kv0 = u[4], kv1 = u[5], ws_row = u[6];
   const int* rq = p.reqs + 4 * r;

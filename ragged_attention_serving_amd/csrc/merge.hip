@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   constexpr int RPW = 64 / L;     // rows per wave
   const int lane = threadIdx.x & 63;
   const int item = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / L;
-  if (item >= p.num_merges) return;
+  if (item >= (p.merge_count ? *p.merge_count : p.num_merges)) return;
   const int sub = lane % L;       // dims 4sub .. 4sub+3
   const int4 mi = *reinterpret_cast<const int4*>(p.merges + 4 * static_cast<int64_t>(item));
   const int out_row = mi.x, ws0 = mi.y, nch = mi.z, stride = mi.w;

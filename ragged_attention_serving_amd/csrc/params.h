@@ -19,7 +19,12 @@ struct AttnParams {
   const int32_t* units; // [n][8]: r, hk, row0, nrows, kv0, kv1, ws_row, cost
   const int32_t* pages; // [total_pages] physical page per logical page; nullptr: identity
   const int32_t* merges;// [m][4]: out_row, ws_row0, nchunks, stride
-  int32_t num_units;
+  // graph-stable launches: the grid is the slot's capacity and these device words hold
+  // the plan's unit count of the launched family and its merge count (nullptr: the grid
+  // size is the count)
+  const int32_t* unit_count;
+  const int32_t* merge_count;
+  int32_t num_units;    // grid size of an attention launch
   int32_t num_merges;
   int32_t hq, hkv, d, group;
   int32_t page_size;

@@ -88,3 +88,84 @@ def test_captured_run_replays_its_plan(gpu):
     compare(from_device(o2), l2.cpu().numpy().astype(np.float64), r2, rl2, "bf16", label="next plan")
     del g
     plan.close()
+
+
+def _pool_batch(rng, pool_pages, qo_lens, kv_lens, page_size):
+    """A batch's packing over a shared page pool: pages drawn without replacement."""
+    npages = [(k + page_size - 1) // page_size for k in kv_lens]
+    kv_indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+    pages = rng.choice(pool_pages, size=int(kv_indptr[-1]), replace=False).astype(np.int32)
+    last = np.array([k - (n - 1) * page_size if n else page_size for k, n in zip(kv_lens, npages)], np.int32)
+    qo_indptr = np.concatenate([[0], np.cumsum(qo_lens)]).astype(np.int32)
+    return qo_indptr, kv_indptr, pages, last
+
+
+def test_graph_stable_replays_across_plans(gpu):
+    """With XATTN_PLAN_GRAPH_STABLE, one captured graph per slot replays later schedules of
+    other shapes: every replay equals an eager run bit for bit and matches the oracle."""
+    import torch
+    import ragged_attention_serving_amd as xa
+    hq, hkv, d, ps = 8, 2, 128, 16
+    rng = np.random.default_rng(90)
+    pool_pages = 3000
+    k_np = synth.normal_tensor((pool_pages, ps, hkv, d), 90, synth.TENSOR_K, "bf16")
+    v_np = synth.normal_tensor((pool_pages, ps, hkv, d), 90, synth.TENSOR_V, "bf16")
+    # the first two plans (one per slot) set the capacities: decode rows (1 and 2 tokens, so 4
+    # and 8 rows), a split long context (merges) and multi-token tiles; later ones are smaller
+    batches = [([1, 2, 1, 40, 130], [20000, 3000, 700, 300, 200]),
+               ([2, 1, 1, 60, 100], [15000, 9000, 900, 500, 260]),
+               ([1, 1, 37], [12000, 100, 90]),
+               ([1, 2, 1, 1], [18000, 40, 5000, 16]),
+               ([90, 1], [150, 16000]),
+               ([1, 1, 1, 3], [1, 17, 10000, 64])]
+    max_q = max(sum(q) for q, _ in batches)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        k = to_device(k_np, "bf16", gpu)
+        v = to_device(v_np, "bf16", gpu)
+        qbuf = torch.zeros((max_q, hq, d), dtype=torch.bfloat16, device=gpu)
+        obuf = torch.zeros_like(qbuf)
+        lbuf = torch.zeros((max_q, hq), dtype=torch.float32, device=gpu)
+    plan = xa.Plan(graph_stable=True)
+    graphs, gens = {}, {}
+    for step, (qo_lens, kv_lens) in enumerate(batches):
+        qo_indptr, kv_indptr, pages, last = _pool_batch(rng, pool_pages, qo_lens, kv_lens, ps)
+        nq = int(qo_indptr[-1])
+        q_np = synth.round_to_bf16_bits(rng.standard_normal((nq, hq, d)).astype(np.float32))
+        with torch.cuda.stream(s):
+            plan.plan(qo_indptr, kv_indptr, pages, last, hq, hkv, d, ps, pool_pages, 1, stream=s)
+            qbuf[:nq].copy_(to_device(q_np, "bf16", gpu))
+            obuf.zero_()
+            lbuf.zero_()
+        s.synchronize()
+        info = plan.info()
+        slot, gen = info["slot"], info["layout_generation"]
+        log(f"  step {step}: slot {slot} generation {gen} units {info['num_units']} merges {info['num_merge_rows']}")
+        qv, ov, lv = qbuf[:nq], obuf[:nq], lbuf[:nq]
+        if slot not in graphs:
+            with torch.cuda.stream(s):
+                plan.run(qv, k, v, ov, lv, stream=s)  # eager warm-up before the capture
+            s.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                plan.run(qv, k, v, ov, lv, stream=s)
+            s.synchronize()
+            graphs[slot], gens[slot] = g, gen
+            with torch.cuda.stream(s):
+                obuf.zero_()
+                lbuf.zero_()
+            s.synchronize()
+        else:
+            assert gen == gens[slot], "a smaller schedule must keep the slot's layout"
+        graphs[slot].replay()
+        s.synchronize()
+        with torch.cuda.stream(s):
+            eo, el = plan.run(qv, k, v, stream=s)
+        s.synchronize()
+        assert np.array_equal(_bits(ov), _bits(eo)), f"step {step}: replay differs from the eager run"
+        assert np.array_equal(lv.cpu().numpy(), el.cpu().numpy()), f"step {step}: lse differs"
+        ro, rl = ref.paged_attention(q_np, k_np, v_np, qo_indptr, kv_indptr, pages, last, hq, hkv, ps,
+                                     dtype="bf16", mask_mode=1)
+        compare(from_device(ov), lv.cpu().numpy().astype(np.float64), ro, rl, "bf16", label=f"step {step} replay")
+    del graphs
+    plan.close()

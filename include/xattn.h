@@ -115,6 +115,12 @@ enum xattn_status {
  *
  * On error the handle (if any) keeps its previous schedule unchanged.
  */
+XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+               const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
+               int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
+               int32_t block_size, float sm_scale, int32_t dtype, void* stream);
+
 enum xattn_plan_flags {
   XATTN_PLAN_GRAPH_STABLE = 1
 };
@@ -137,12 +143,6 @@ enum xattn_plan_flags {
  * match each schedule exactly.
  */
 XATTN_API int xattn_plan_create(xattn_plan_t* plan, int32_t flags);
-
-XATTN_API int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
-               const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
-               int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
-               int32_t head_dim, int32_t page_size, int64_t num_pages, int32_t mask_mode,
-               int32_t block_size, float sm_scale, int32_t dtype, void* stream);
 
 /*
  * xattn_run: one layer's attention with the latest schedule (page

@@ -178,7 +178,13 @@ def summarize(w, m):
         res["TFLOPs_cold"] = flops / (m["cold_ms"] * 1e-3) / 1e12 if m["cold_ms"] else None
         res["kernel_TFLOPs"] = flops / (per[dominant] * 1e-3) / 1e12 if dominant else None
         res["mfma_frac"] = res["kernel_TFLOPs"] / peak if dominant else None
-        res["hbm_GBps_compulsory"] = kv_bytes / (per[dominant] * 1e-3) / 1e9 if dominant else None
+        # compulsory HBM bytes of a prefill: K and V once, Q read and out and lse written once
+        elt = 2 if w.dtype == "bf16" else 4
+        rows = int(w.qo_lens().sum()) * w.num_qo_heads
+        hbm_bytes = kv_bytes + rows * (2 * w.head_dim * elt + 4)
+        res["hbm_bytes_compulsory"] = hbm_bytes
+        res["hbm_GBps_compulsory"] = hbm_bytes / (per[dominant] * 1e-3) / 1e9 if dominant else None
+        res["hbm_frac_compulsory"] = res["hbm_GBps_compulsory"] / HBM_PEAK_GBS if dominant else None
     return res
 
 

@@ -82,6 +82,7 @@ struct Slot {
   std::vector<int64_t> layout_key;
   int64_t layout_gen = 0;
   int32_t dtype = 0, hq = 0, hkv = 0, d = 0, page_size = 0, mask = 0, block = 0;
+  int64_t pool_bytes = 0;  // bytes of each of the K and V pools
 };
 
 }  // namespace
@@ -338,6 +339,8 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
   sl.page_size = page_size;
   sl.mask = mask_mode;
   sl.block = block_size;
+  sl.pool_bytes = num_pages * page_size * static_cast<int64_t>(num_kv_heads) * head_dim *
+                  (dtype == XATTN_BF16 ? 2 : 4);
   // what a run launches: this schedule's kernels, or in a graph-stable handle the union
   // over the slot's plans (a launch whose count is 0 this time exits at once)
   int fams = 0;
@@ -353,7 +356,8 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
       static_cast<int64_t>(off_reqs), static_cast<int64_t>(off_merges), static_cast<int64_t>(off_pages),
       static_cast<int64_t>(off_kv_start), static_cast<int64_t>(sl.cap_merges), sl.run_fams,
       sl.run_merge, sl.run_dec_rows, s.identity, s.group, s.tile_rows, dtype, num_qo_heads,
-      num_kv_heads, head_dim, page_size, mask_mode, block_size};
+      num_kv_heads, head_dim, page_size, mask_mode, block_size,
+      sl.pool_bytes > 0 && sl.pool_bytes <= static_cast<int64_t>(UINT32_MAX)};  // the tile kernel's load form
   for (int f = 0; f < xattn::FAM_COUNT; ++f) {
     key.push_back(static_cast<int64_t>(off_units[f]));
     key.push_back(static_cast<int64_t>(sl.cap_units[f]));
@@ -462,6 +466,7 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   p.tile_rows = s.tile_rows;
   p.scale = s.scale;
   p.scale_log2 = s.scale * 1.4426950408889634f;
+  p.pool_bytes = sl.pool_bytes;
 
   // optional per-kernel events (xattn_plan_set_timing)
   const bool timed = plan->timing_every > 0 && plan->runs++ % plan->timing_every == 0 &&

@@ -3,9 +3,11 @@
 // One workgroup (NW = 4 or 8 waves) per unit: a request's KV head, up to 32 * NW query
 // rows (32 per wave), and a KV range walked in tiles of 64 keys.
 //
-// Data movement. K and V tiles go straight from HBM to LDS with the 16-byte
-// global->LDS loads (no register staging), double buffered: tile j+1 loads while tile
-// j computes. Both keep their natural row layout (key rows of head_dim values) with
+// Data movement. K and V tiles go straight from HBM to LDS with 16-byte loads that
+// write LDS directly (no register staging), double buffered: tile j+1 loads while tile
+// j computes. When the pools span less than 4 GB the loads are buffer loads whose
+// per-lane offsets are 32-bit (the pool base sits in scalar registers); larger pools
+// take global loads with 64-bit addresses. Both keep their natural row layout (key rows of head_dim values) with
 // the 16-byte chunks of each row XOR-swizzled by the row, so that the MFMA operand
 // reads below hit distinct LDS banks. The page indices of the unit's pages are staged
 // in LDS once, so the tile loop issues no vector-memory operation other than the tile
@@ -72,7 +74,7 @@ __device__ __forceinline__ void block_barrier() {
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-template <int D, int MASK, int NW, int BN>
+template <int D, int MASK, int NW, int BN, bool BUF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p) {
   using C = Cfg<D, NW, BN>;
   constexpr int NKB = C::NKB, NST = C::NST;
@@ -94,6 +96,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   const int g = p.group;
   const char* kbytes = static_cast<const char*>(p.k);
   const char* vbytes = static_cast<const char*>(p.v);
+  // buffer form: no range limit beyond the 32-bit offsets (like the global form)
+  const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.k), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.v), (short)0, -1, 0x00020000);
 
   // this lane's query column
   const int lrow = 32 * wave + col;
@@ -141,14 +146,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   // ---- global -> LDS loads of tile j: this wave fills NIW 1 KB blocks of the K tile and
   // the same blocks of the V tile. The byte offsets in the pool (shared by K and V) come
   // from the tile's row ids, the row of key k being held by lane k.
+  using Off = typename std::conditional<BUF, uint32_t, int64_t>::type;
   struct TileOffsets {
-    int64_t v[C::NIW];
+    Off v[C::NIW];
   };
   // identity table: key t of the request is pool row page_base * page_size + t, so a
   // lane's offsets for tile j are those of tile 0 plus j whole tiles, except in a last
   // tile that runs past the range (its keys clamp to the range's last key)
   TileOffsets id_base;
-  const int64_t id_stride = static_cast<int64_t>(BN) * p.hkv * C::ROWB;
+  const Off id_stride = static_cast<Off>(BN) * p.hkv * C::ROWB;
   auto identity_offsets = [&](int j) __attribute__((always_inline)) -> TileOffsets {
     TileOffsets t;
 #pragma unroll
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
       const int key = C::RPI * n + lane / C::LPR;  // key row this lane fills
       const int src16 = (lane % C::LPR) ^ C::swz(key);  // global chunk for this slot
       const int row = (page_base * p.page_size + min(kv0 + j * BN + key, kv1 - 1)) * p.hkv + hk;
-      t.v[i] = static_cast<int64_t>(static_cast<uint32_t>(row)) * C::ROWB + 16 * src16;
+      t.v[i] = static_cast<Off>(static_cast<uint32_t>(row)) * C::ROWB + 16 * src16;
     }
     return t;
   };
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     TileOffsets t;
     if (!paged) {
       if (kv0 + (j + 1) * BN > kv1) return identity_offsets(j);
-      const int64_t add = id_stride * j;
+      const Off add = id_stride * j;
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) t.v[i] = id_base.v[i] + add;
       return t;
@@ -177,22 +183,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
       const int n = C::NIW * wave + i;
       const int key = C::RPI * n + lane / C::LPR;
       const int src16 = (lane % C::LPR) ^ C::swz(key);
-      t.v[i] = static_cast<int64_t>(static_cast<uint32_t>(__shfl(rh, key, 64))) * C::ROWB + 16 * src16;
+      t.v[i] = static_cast<Off>(static_cast<uint32_t>(__shfl(rh, key, 64))) * C::ROWB + 16 * src16;
     }
     return t;
   };
-  auto issue_one = [&](const char* src, lds_char* dst, const TileOffsets& t, int i) __attribute__((always_inline)) {
-    // (both addresses are variables of their own: with template-dependent expressions in
-    // the builtin's arguments, the host compilation pass silently drops the kernel's
+  // `which`: 0 loads from the K pool, 1 from the V pool
+  auto issue_one = [&](auto which, lds_char* dst, const TileOffsets& t, int i) __attribute__((always_inline)) {
+    // (every address is a variable of its own: with template-dependent expressions in
+    // the builtins' arguments, the host compilation pass silently drops the kernel's
     // launch stub)
     const int n = C::NIW * wave + i;
-    const char* g = src + t.v[i];
-    __builtin_amdgcn_global_load_lds(g, dst + n * 1024, 16, 0, 0);
+    lds_char* d = dst + n * 1024;
+    if constexpr (BUF) {
+      const uint32_t off = t.v[i];
+      const __amdgpu_buffer_rsrc_t rs = decltype(which)::value ? rsv : rsk;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, off, 0, 0, 0);
+    } else {
+      const char* g = (decltype(which)::value ? vbytes : kbytes) + t.v[i];
+      __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
+    }
   };
-  auto issue = [&](const char* src, lds_char* dst, int j) __attribute__((always_inline)) {
+  using PoolK = std::integral_constant<int, 0>;
+  using PoolV = std::integral_constant<int, 1>;
+  auto issue = [&](auto which, lds_char* dst, int j) __attribute__((always_inline)) {
     const TileOffsets t = tile_offsets(j);
 #pragma unroll
-    for (int i = 0; i < C::NIW; ++i) issue_one(src, dst, t, i);
+    for (int i = 0; i < C::NIW; ++i) issue_one(which, dst, t, i);
   };
 
   // ---- per-lane LDS read offsets (bytes within a buffer), fixed for the unit.
@@ -237,8 +253,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
 
   // ---- prologue: tile 0 in LDS
   if (ntiles > 0) {
-    issue(kbytes, (lds_char*)sk0, 0);
-    issue(vbytes, (lds_char*)sv0, 0);
+    issue(PoolK{}, (lds_char*)sk0, 0);
+    issue(PoolV{}, (lds_char*)sv0, 0);
   }
   wait_all_loads();
   block_barrier();
@@ -257,9 +273,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     if (more) nxt = tile_offsets(j + 1);
     if (!wave_active && more) {
 #pragma unroll
-      for (int i = 0; i < C::NIW; ++i) issue_one(kbytes, knext, nxt, i);
+      for (int i = 0; i < C::NIW; ++i) issue_one(PoolK{}, knext, nxt, i);
 #pragma unroll
-      for (int i = 0; i < C::NIW; ++i) issue_one(vbytes, vnext, nxt, i);
+      for (int i = 0; i < C::NIW; ++i) issue_one(PoolV{}, vnext, nxt, i);
     }
     if (wave_active) {
       // S^T = K Q^T for the tile's 32-key blocks; accumulator i of block kb holds key
@@ -290,8 +306,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
 #pragma unroll
           for (int x = 0; x < PER_KK; ++x) {
             const int i = kk * PER_KK + x;
-            if (i < C::NIW) issue_one(kbytes, knext, nxt, i);
-            else if (i < 2 * C::NIW) issue_one(vbytes, vnext, nxt, i - C::NIW);
+            if (i < C::NIW) issue_one(PoolK{}, knext, nxt, i);
+            else if (i < 2 * C::NIW) issue_one(PoolV{}, vnext, nxt, i - C::NIW);
           }
         }
       }
@@ -400,15 +416,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   }
 }
 
-template <int D, int NW, int BN>
-hipError_t launch_dw(const AttnParams& p, const Launch& l) {
+template <int D, int NW, int BN, bool BUF>
+hipError_t launch_dwb(const AttnParams& p, const Launch& l) {
   const dim3 grid(p.num_units), block(64 * NW);
   switch (p.mask) {
-    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW, BN>, grid, block, p, l);
-    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW, BN>, grid, block, p, l);
-    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW, BN>, grid, block, p, l);
+    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW, BN, BUF>, grid, block, p, l);
+    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW, BN, BUF>, grid, block, p, l);
+    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW, BN, BUF>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
+}
+
+// buffer loads (32-bit offsets) when both pools span less than 4 GB
+template <int D, int NW, int BN>
+hipError_t launch_dw(const AttnParams& p, const Launch& l) {
+  if (buffer_loads_fit(p)) return launch_dwb<D, NW, BN, true>(p, l);
+  return launch_dwb<D, NW, BN, false>(p, l);
 }
 
 constexpr int kTileKeys = 64;  // keys per K/V tile

@@ -33,6 +33,13 @@ struct AttnParams {
   int32_t tile_rows;    // query rows per MFMA tile unit (128 or 256)
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
+  int64_t pool_bytes;   // bytes of each of the K and V pools (num_pages * page_size * hkv * d * elt)
 };
+
+// The tile kernel addresses K and V with 32-bit offsets from the pool base when the pools
+// span less than 4 GB (every offset then fits).
+inline bool buffer_loads_fit(const AttnParams& p) {
+  return p.pool_bytes > 0 && p.pool_bytes <= static_cast<int64_t>(UINT32_MAX);
+}
 
 }  // namespace xattn

@@ -4,6 +4,7 @@
   decode and the tile kernels, paged and identity tables.
 - Many requests, wide head groups, and the largest decode row count.
 - Argument errors that the library must report without launching anything.
+- K and V pools past 4 GB each (64-bit addressing in the tile kernel).
 """
 import ctypes
 
@@ -12,7 +13,7 @@ import pytest
 
 from oracle import ref
 from ragged_attention_serving_amd import synth
-from tests.gpu_util import compare, log, run_gpu, to_device
+from tests.gpu_util import compare, forced_chunk, from_device, log, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +96,38 @@ def test_argument_errors_are_reported(gpu):
     ro, rl = ref.run_workload(w)
     compare(from_device(o), l.cpu().numpy().astype(np.float64), ro, rl, "bf16", label="after a failed plan")
     plan.close()
+
+
+def test_pools_past_4_gb(gpu):
+    """K and V pools of more than 4 GB each: the tile kernel leaves its 32-bit buffer offsets
+    for 64-bit addresses, and every kernel reads pages beyond the first 4 GB."""
+    import torch
+    import ragged_attention_serving_amd as xa
+    # MFMA tiles (prefill rows), decode rows and a split long context, causal GQA
+    w = synth.paged_case([100, 1, 37, 2], [700, 900, 300, 5000], 8, 2, 128, 16, mask_mode=1, seed=87,
+                         name="pool_past_4gb")
+    page_bytes = w.page_size * w.num_kv_heads * w.head_dim * 2
+    big = (1 << 32) // page_bytes + 4096  # pages: the pools span 4 GB + 32 MB each
+    base = big - w.num_pages              # the workload's pages sit at the top
+    log(f"[limits] pools of {big} pages ({big * page_bytes / 2**30:.2f} GiB each), pages from {base}")
+    k = torch.empty((big, w.page_size, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device=gpu)
+    v = torch.empty_like(k)
+    k[base:] = to_device(w.k_pages, "bf16", gpu)
+    v[base:] = to_device(w.v_pages, "bf16", gpu)
+    q = to_device(w.q, "bf16", gpu)
+    pages = (w.kv_page_indices.astype(np.int64) + base).astype(np.int32)
+    for chunk in (0, 512):
+        plan = xa.Plan()
+        with forced_chunk(chunk):
+            plan.plan(w.qo_indptr, w.kv_indptr, pages, w.kv_last_page_len, w.num_qo_heads, w.num_kv_heads,
+                      w.head_dim, w.page_size, big, w.mask_mode)
+        info = plan.info()
+        log(f"  chunk {chunk}: schedule {info}")
+        assert info["num_units"][2] > 0 and info["num_units"][1] > 0
+        o, l = plan.run(q, k, v)
+        torch.cuda.synchronize()
+        ro, rl = ref.run_workload(w)  # the same pages in a compact pool
+        compare(from_device(o), l.cpu().numpy().astype(np.float64), ro, rl, "bf16", label=f"{w.name} chunk {chunk}")
+        plan.close()
+    del k, v
+    torch.cuda.empty_cache()

@@ -168,6 +168,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     return t;
   };
   if (!paged) id_base = identity_offsets(0);
+  // paged, buffer form, keys from a page boundary on and pages a multiple of a load's rows:
+  // the rows of one 1 KB load lie in one page, so a lane's offset in a whole tile is that
+  // page's start (its index read from LDS) plus a constant of the unit
+  const bool pg_whole = BUF && paged && p.page_shift >= 0 && (BN & (p.page_size - 1)) == 0 &&
+                        (p.page_size % C::RPI) == 0 && (kv0 & (p.page_size - 1)) == 0;
+  const uint32_t pg_bytes = static_cast<uint32_t>(p.page_size * p.hkv * C::ROWB);
+  uint32_t pg_const[C::NIW];
+#pragma unroll
+  for (int i = 0; i < C::NIW; ++i) {
+    const int key = C::RPI * (C::NIW * wave + i) + lane / C::LPR;
+    const int src16 = (lane % C::LPR) ^ C::swz(key);
+    pg_const[i] = static_cast<uint32_t>((((key & (p.page_size - 1)) * p.hkv + hk) * C::ROWB) + 16 * src16);
+  }
   auto tile_offsets = [&](int j) __attribute__((always_inline)) -> TileOffsets {
     TileOffsets t;
     if (!paged) {
@@ -175,6 +188,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
       const Off add = id_stride * j;
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) t.v[i] = id_base.v[i] + add;
+      return t;
+    }
+    if (pg_whole && kv0 + (j + 1) * BN <= kv1) {
+#pragma unroll
+      for (int i = 0; i < C::NIW; ++i) {
+        const int key = C::RPI * (C::NIW * wave + i) + lane / C::LPR;
+        const uint32_t page = static_cast<uint32_t>(spg[(j * BN + key) >> p.page_shift]);
+        t.v[i] = static_cast<Off>(page * pg_bytes + pg_const[i]);
+      }
       return t;
     }
     const int rh = tile_row_head(j);

@@ -290,10 +290,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     lds_char* vcur = (lds_char*)(P == 0 ? sv0 : sv1);
     lds_char* knext = (lds_char*)(P == 0 ? sk1 : sk0);
     lds_char* vnext = (lds_char*)(P == 0 ? sv1 : sv0);
-    const bool more = j + 1 < ntiles;
-    TileOffsets nxt{};
-    if (more) nxt = tile_offsets(j + 1);
-    if (!wave_active && more) {
+    // the last step reloads its own tile into the free buffer (an L2 hit that nothing
+    // reads), so that no load sits behind a branch
+    const TileOffsets nxt = tile_offsets(j + 1 < ntiles ? j + 1 : j);
+    if (!wave_active) {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) issue_one(PoolK{}, knext, nxt, i);
 #pragma unroll
@@ -324,13 +324,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][kk], qb[kk], sc[kb], 0, 0, 0);
-        if (more) {
 #pragma unroll
-          for (int x = 0; x < PER_KK; ++x) {
-            const int i = kk * PER_KK + x;
-            if (i < C::NIW) issue_one(PoolK{}, knext, nxt, i);
-            else if (i < 2 * C::NIW) issue_one(PoolV{}, vnext, nxt, i - C::NIW);
-          }
+        for (int x = 0; x < PER_KK; ++x) {
+          const int i = kk * PER_KK + x;
+          if (i < C::NIW) issue_one(PoolK{}, knext, nxt, i);
+          else if (i < 2 * C::NIW) issue_one(PoolV{}, vnext, nxt, i - C::NIW);
         }
       }
 

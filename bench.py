@@ -41,6 +41,30 @@ KERNEL_SOURCES = {
     "write": "ragged_attention_serving_amd/csrc/write_kv.hip",
 }
 TIMING_EVERY = 5  # kernel start/end events on every 5th timed run
+# Without --warmup, warm-up runs continue until this much time has passed: the GPU leaves
+# its idle clocks only after some tens of milliseconds of load (a short prefill timed at
+# once reads about 25% slow).
+WARMUP_SECONDS = 0.5
+MAX_AUTO_WARMUP = 4000
+
+
+def warm_up(run, warmup):
+    """Runs `run` `warmup` times, or (warmup None) until WARMUP_SECONDS have passed (at least
+    5 runs); returns the number of runs."""
+    import torch
+    if warmup is not None:
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        return warmup
+    n = 0
+    t0 = time.perf_counter()
+    while n < 5 or (time.perf_counter() - t0 < WARMUP_SECONDS and n < MAX_AUTO_WARMUP):
+        for _ in range(5):
+            run()
+        n += 5
+        torch.cuda.synchronize()
+    return n
 KERNEL_NAMES = {"decode": "attn_decode_kernel", "mfma": "attn_mma_kernel", "fp32": "attn_f32_kernel",
                 "merge": "merge_kernel"}
 
@@ -89,9 +113,7 @@ def measure(w, steps, warmup, dev, cold_steps=5):
               w.sm_scale, w.dtype)
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info()
-    for _ in range(warmup):
-        plan.run(q, k, v, out, lse)
-    torch.cuda.synchronize()
+    warmed = warm_up(lambda: plan.run(q, k, v, out, lse), warmup)
 
     # timed region: exactly `steps` runs, synchronised on both sides; on every TIMING_EVERY-th
     # run the library launches each kernel with HIP events stamped with its start and end,
@@ -120,7 +142,7 @@ def measure(w, steps, warmup, dev, cold_steps=5):
     del scratch
     plan.close()
     del q, k, v, out, lse
-    return dict(plan_ms=plan_ms, wall_ms=wall_ms, stages=stages, info=info,
+    return dict(plan_ms=plan_ms, wall_ms=wall_ms, stages=stages, info=info, warmup=warmed,
                 cold_ms=float(np.median(cold)) if cold else None)
 
 
@@ -141,9 +163,7 @@ def measure_write(w, steps, warmup, dev):
     plan.plan(w.qo_indptr, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, w.num_qo_heads,
               w.num_kv_heads, w.head_dim, w.page_size, w.num_pages, w.mask_mode, w.block_size,
               w.sm_scale, w.dtype)
-    for _ in range(warmup):
-        plan.write_kv(ksrc, vsrc, kpool, vpool)
-    torch.cuda.synchronize()
+    warmed = warm_up(lambda: plan.write_kv(ksrc, vsrc, kpool, vpool), warmup)
     t0 = time.perf_counter()
     for _ in range(steps):
         plan.write_kv(ksrc, vsrc, kpool, vpool)
@@ -151,7 +171,7 @@ def measure_write(w, steps, warmup, dev):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     moved = 2 * 2 * ksrc.numel() * ksrc.element_size()
     plan.close()
-    return {"workload": f"context_write:{w.name}", "ms_per_write": round(ms, 5),
+    return {"workload": f"context_write:{w.name}", "ms_per_write": round(ms, 5), "warmup": warmed,
             "bytes": moved, "GBps": moved / (ms * 1e-3) / 1e9,
             "hbm_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -258,8 +278,9 @@ def cpu_baseline(w, cpu_seconds=24.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed runs before the timed ones (default: as many as fill %.1f s)" % WARMUP_SECONDS)
     ap.add_argument("--workload", default="whisper_decode_cross")
     ap.add_argument("--all", action="store_true", help="also measure every other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -330,7 +351,7 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 5), "higher_is_better": True,
+        "warmup": m["warmup"], "ms_per_step": round(res["ms_per_step"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "requests": w.batch_size, "query_tokens": int(w.qo_indptr[-1]),
                    "kv_tokens": int(w.kv_lens().sum()), "num_qo_heads": w.num_qo_heads,
@@ -351,9 +372,10 @@ def main():
             log(f"[bench] sweep: generating {name}")
             ws = fn(0)
             log(f"[bench] sweep: measuring {name}")
-            ms = measure(ws, max(5, min(args.steps, 20)), 3, dev)
+            ms = measure(ws, args.steps, None, dev)
             r = summarize(ws, ms)
             r.pop("schedule", None)
+            r["warmup"] = ms["warmup"]
             sweep[name] = r
             log(f"[bench] {json.dumps(r)}")
             del ws, ms
@@ -362,15 +384,16 @@ def main():
             log(f"[bench] sweep: generating {name}")
             ws = fn(0)
             log(f"[bench] sweep: measuring {name}")
-            ms = measure(ws, max(5, min(args.steps, 20)), 3, dev)
+            ms = measure(ws, args.steps, None, dev)
             r = summarize(ws, ms)
             r.pop("schedule", None)
+            r["warmup"] = ms["warmup"]
             sweep[name] = r
             log(f"[bench] {json.dumps(r)}")
             del ws, ms
             torch.cuda.empty_cache()
         log("[bench] sweep: context write")
-        wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), max(5, min(args.steps, 20)), 3, dev)
+        wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), args.steps, None, dev)
         sweep[wr["workload"]] = wr
         log(f"[bench] {json.dumps(wr)}")
         line["sweep"] = sweep

@@ -94,6 +94,12 @@ SMALL = [
     ("mma_block_d128", [300, 65, 1], [300, 65, 1], 2, 2, 128, 1, 2, 64, "bf16"),
     ("mma_block_odd", [100, 250], [130, 250], 2, 1, 64, 5, 2, 7, "bf16"),
     ("mma_page3", [50, 10], [77, 30], 2, 2, 64, 3, 0, 0, "bf16"),
+    # page sizes around the tile kernel's whole-page addressing (a 1 KB load spans 8 rows at
+    # head_dim 64 and 4 at 128; tiles are 64 keys)
+    ("mma_page8_d64", [70, 3], [200, 90], 2, 2, 64, 8, 0, 0, "bf16"),
+    ("mma_page4_d128_causal", [40, 130], [100, 131], 4, 2, 128, 4, 1, 0, "bf16"),
+    ("mma_page64_d64", [33, 140], [500, 140], 2, 2, 64, 64, 1, 0, "bf16"),
+    ("mma_page128_d128", [20, 9], [300, 129], 2, 2, 128, 128, 0, 0, "bf16"),
     ("f32_all_masks_none", [1, 5, 2], [16, 40, 7], 2, 2, 16, 4, 0, 0, "f32"),
     ("f32_causal_gqa", [3, 1, 6], [7, 13, 6], 4, 1, 32, 3, 1, 0, "f32"),
     ("f32_block_d64", [10, 17], [10, 17], 2, 2, 64, 1, 2, 4, "f32"),

@@ -7,12 +7,11 @@
 // write LDS directly (no register staging), double buffered: tile j+1 loads while tile
 // j computes. When the pools span less than 4 GB the loads are buffer loads whose
 // per-lane offsets are 32-bit (the pool base sits in scalar registers); larger pools
-// take global loads with 64-bit addresses. Both keep their natural row layout (key rows of head_dim values) with
-// the 16-byte chunks of each row XOR-swizzled by the row, so that the MFMA operand
-// reads below hit distinct LDS banks. The page indices of the unit's pages are staged
-// in LDS once, so the tile loop issues no vector-memory operation other than the tile
-// loads themselves.
-
+// take global loads with 64-bit addresses. Both tiles keep their natural row layout
+// (key rows of head_dim values) with the 16-byte chunks of each row XOR-swizzled by the
+// row, so that the MFMA operand reads below hit distinct LDS banks. The page indices of
+// the unit's pages are staged in LDS once, so the tile loop issues no vector-memory
+// operation other than the tile loads themselves.
 //
 // Math, per tile and wave:
 //   * S^T = K Q^T (keys x the wave's 32 query columns) with Q held in registers as the

@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -73,11 +74,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """The source without comments and blank lines: edits to comments keep the hash."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", l).rstrip() for l in text.splitlines())
+    return "\n".join(l for l in lines if l.strip())
+
+
 def source_sha(stage: str) -> str:
+    """Hash of the code (comments stripped) of a kernel stage's source and device.h."""
     h = hashlib.sha256()
     for rel in (KERNEL_SOURCES[stage], "ragged_attention_serving_amd/csrc/device.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,0 +1,51 @@
+"""GPU parity over seeded random shapes: head counts and groups, head dims, page sizes,
+masks, query and context lengths, forced chunk lengths, and both tile heights. Each case
+is small enough for the oracle; together they cross the kernels' addressing paths (whole
+pages or per-row tables, buffer or global loads) with ragged tails."""
+import numpy as np
+import pytest
+
+from oracle import ref
+from ragged_attention_serving_amd import synth
+from tests.gpu_util import compare, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 40
+
+
+def _case(i):
+    rng = np.random.default_rng(1000 + i)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    ps = int(rng.choice([1, 2, 3, 4, 8, 16, 32, 64, 128]))
+    mask = int(rng.integers(0, 3))
+    b = int(rng.integers(1, 6))
+    kv = rng.integers(1, 700, b)
+    decode_like = rng.random() < 0.4  # one or two query tokens: the decode kernel's rows
+    hi = 3 if decode_like else 160
+    if mask == 0:
+        qo = rng.integers(0 if not decode_like else 1, hi, b)
+    else:
+        qo = np.minimum(rng.integers(1, hi, b), kv)
+    block = int(rng.choice([1, 7, 16, 64])) if mask == 2 else 0
+    chunk = int(rng.choice([0, 0, 64, 100, 257]))
+    rows = int(rng.choice([128, 256]))
+    w = synth.paged_case(qo, kv, hkv * g, hkv, d, ps, mask_mode=mask, block_size=block, seed=2000 + i,
+                         name=f"random_{i}", extra_pages=int(rng.integers(0, 5)))
+    return w, chunk, rows
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_shape(i, gpu, monkeypatch):
+    w, chunk, rows = _case(i)
+    monkeypatch.setenv("XATTN_TILE_ROWS", str(rows))
+    log(f"[random] case {i}: hq {w.num_qo_heads} hkv {w.num_kv_heads} d {w.head_dim} page {w.page_size} "
+        f"mask {w.mask_mode} block {w.block_size} qo {list(np.diff(w.qo_indptr))} "
+        f"kv {list(w.kv_lens())} chunk {chunk} rows {rows}")
+    out, lse, plan = run_gpu(w, gpu, chunk)
+    log(f"  schedule {plan.info()}")
+    ro, rl = ref.run_workload(w)
+    compare(out, lse, ro, rl, w.dtype, label=w.name)
+    plan.close()

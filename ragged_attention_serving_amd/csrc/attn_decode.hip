@@ -246,7 +246,6 @@ hipError_t launch_rows(const AttnParams& p, int rows, const Launch& l) {
     case 1: return launch_kernel(attn_decode_kernel<D, 1>, grid, block, p, l);
     case 2: return launch_kernel(attn_decode_kernel<D, 2>, grid, block, p, l);
     case 4: return launch_kernel(attn_decode_kernel<D, 4>, grid, block, p, l);
-    case 8: return launch_kernel(attn_decode_kernel<D, 8>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
 }

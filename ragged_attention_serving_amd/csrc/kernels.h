@@ -25,7 +25,7 @@ hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, const AttnParams&
 
 // fp32 storage and arithmetic, any mask, head_dim 16/32/64/128; units of <= 4 rows.
 hipError_t launch_attn_f32(const AttnParams& p, const Launch& l);
-// bf16 decode: units of up to `rows` query rows sharing one KV head (rows in 1,2,4,8).
+// bf16 decode: units of up to `rows` query rows sharing one KV head (rows in 1, 2, 4).
 hipError_t launch_attn_decode(const AttnParams& p, int rows, const Launch& l);
 // bf16 MFMA tiles: units of up to 128 query rows sharing one KV head.
 hipError_t launch_attn_mma(const AttnParams& p, const Launch& l);

@@ -13,7 +13,10 @@ enum Family { FAM_F32 = 0, FAM_DEC = 1, FAM_MMA = 2, FAM_COUNT = 3 };
 
 // Rows (query tokens x grouped heads) per unit for each family.
 constexpr int kF32Rows = 4;    // fp32 kernel: scores of a chunk kept in LDS per row
-constexpr int kDecMaxRows = 8; // decode kernel: rows held in registers per lane
+// decode kernel: rows held in registers per lane. Units of 5-8 rows (8 query heads per KV
+// head, or 2 tokens of 4) run faster as query tiles: the decode kernel's VALU work per key
+// grows with its rows while its bytes do not.
+constexpr int kDecMaxRows = 4;
 constexpr int kMmaRows = 128;  // MFMA kernel, default: 4 waves x 32 query columns
 constexpr int kF32MaxChunk = 1024;
 // MFMA kernel: page indices of one unit staged in LDS; a unit may span at most this many pages

@@ -58,10 +58,11 @@ def test_many_short_requests(gpu):
 
 def test_wide_head_groups(gpu):
     # 16 query heads per KV head: a decode token already has 16 rows (tile kernel); 2 tokens of
-    # 4 heads per KV head are the decode kernel's largest unit (8 rows)
+    # 4 heads per KV head are 8 rows (tile kernel too); 1 token of 4 heads, 4 rows, is the
+    # decode kernel's largest unit
     w = synth.paged_case([1, 2, 7], [3000, 500, 900], 32, 2, 128, 16, mask_mode=1, seed=84, name="gqa16")
     _check(w, gpu)
-    w = synth.paged_case([2, 2, 1], [3000, 5, 900], 8, 2, 64, 16, mask_mode=1, seed=85, name="decode_rows8")
+    w = synth.paged_case([2, 2, 1], [3000, 5, 900], 8, 2, 64, 16, mask_mode=1, seed=85, name="rows8_and_rows4")
     _check(w, gpu)
 
 

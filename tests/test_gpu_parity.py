@@ -84,9 +84,9 @@ SMALL = [
     # (name, qo_lens, kv_lens, hq, hkv, d, page_size, mask, block, dtype)
     ("decode_mha_d64", [1] * 9, [1, 2, 15, 16, 17, 100, 513, 1000, 64], 4, 4, 64, 16, 0, 0, "bf16"),
     ("decode_gqa4_causal_d128", [1] * 6, [1, 7, 64, 65, 300, 2049], 8, 2, 128, 16, 1, 0, "bf16"),
-    ("decode_gqa8_d128", [1] * 3, [33, 500, 129], 16, 2, 128, 8, 0, 0, "bf16"),
+    ("gqa8_d128_tiles", [1] * 3, [33, 500, 129], 16, 2, 128, 8, 0, 0, "bf16"),  # 8 rows: tile kernel
     ("decode_rows2_causal", [2, 1, 2], [5, 40, 300], 2, 2, 64, 4, 1, 0, "bf16"),
-    ("decode_rows8_mixed", [2, 4, 1], [9, 70, 33], 4, 2, 64, 3, 1, 0, "bf16"),
+    ("rows8_mixed", [2, 4, 1], [9, 70, 33], 4, 2, 64, 3, 1, 0, "bf16"),  # 4 and 8 rows: decode and tiles
     ("decode_block", [3, 1], [50, 130], 2, 1, 64, 16, 2, 16, "bf16"),
     ("mma_none_d64", [9, 33, 128, 129, 300], [1500, 77, 300, 129, 1000], 2, 2, 64, 16, 0, 0, "bf16"),
     ("mma_causal_d128", [40, 200, 129], [40, 260, 500], 2, 2, 128, 16, 1, 0, "bf16"),

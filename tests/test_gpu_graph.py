@@ -110,11 +110,12 @@ def test_graph_stable_replays_across_plans(gpu):
     pool_pages = 3000
     k_np = synth.normal_tensor((pool_pages, ps, hkv, d), 90, synth.TENSOR_K, "bf16")
     v_np = synth.normal_tensor((pool_pages, ps, hkv, d), 90, synth.TENSOR_V, "bf16")
-    # the first two plans (one per slot) set the capacities: decode rows (1 token, 4 rows; 2
-    # tokens are 8 rows and go to tiles), a split long context (merges) and multi-token tiles;
-    # later ones are smaller
+    # the first two plans (one per slot) set the capacities: decode units (1 token, 4 rows; 2
+    # tokens are 8 rows and go to tiles), split long contexts (merges) and multi-token tiles;
+    # every later plan in the same slot needs no more units of any family, merge rows,
+    # workspace rows, requests or pages
     batches = [([1, 2, 1, 40, 130], [20000, 3000, 700, 300, 200]),
-               ([2, 1, 1, 60, 100], [15000, 9000, 900, 500, 260]),
+               ([1, 1, 1, 60, 100], [20000, 9000, 900, 500, 260]),
                ([1, 1, 37], [12000, 100, 90]),
                ([1, 2, 1, 1], [18000, 40, 5000, 16]),
                ([90, 1], [150, 16000]),

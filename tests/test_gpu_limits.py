@@ -104,8 +104,8 @@ def test_pools_past_4_gb(gpu):
     for 64-bit addresses, and every kernel reads pages beyond the first 4 GB."""
     import torch
     import ragged_attention_serving_amd as xa
-    # MFMA tiles (prefill rows), decode rows and a split long context, causal GQA
-    w = synth.paged_case([100, 1, 37, 2], [700, 900, 300, 5000], 8, 2, 128, 16, mask_mode=1, seed=87,
+    # MFMA tiles (prefill rows), decode rows and split long contexts, causal GQA
+    w = synth.paged_case([100, 1, 37, 1], [700, 9000, 300, 5000], 8, 2, 128, 16, mask_mode=1, seed=87,
                          name="pool_past_4gb")
     page_bytes = w.page_size * w.num_kv_heads * w.head_dim * 2
     big = (1 << 32) // page_bytes + 4096  # pages: the pools span 4 GB + 32 MB each

@@ -4,8 +4,11 @@
 // rows (32 per wave), and a KV range walked in tiles of 64 keys.
 //
 // Data movement. K and V tiles go straight from HBM to LDS with 16-byte loads that
-// write LDS directly (no register staging), double buffered: tile j+1 loads while tile
-// j computes. When the pools span less than 4 GB the loads are buffer loads whose
+// write LDS directly (no register staging), in S stages: tile j+S-1 loads while tile j
+// computes. S is 3 at head_dim 64 (three stages still fit the three workgroups per CU
+// that the registers allow, and keep twice the bytes in flight for short-query units,
+// whose steps are short) and 2 at head_dim 128 (a third stage would leave one
+// workgroup per CU). When the pools span less than 4 GB the loads are buffer loads whose
 // per-lane offsets are 32-bit (the pool base sits in scalar registers); larger pools
 // take global loads with 64-bit addresses. Both tiles keep their natural row layout
 // (key rows of head_dim values) with the 16-byte chunks of each row XOR-swizzled by the
@@ -73,16 +76,25 @@ __device__ __forceinline__ void block_barrier() {
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
+// vmcnt(2 * NIW): every load but the last tile's K and V (NIW each per wave) has landed;
+// vector-memory loads complete in the order they were issued
+template <int NIW>
+__device__ __forceinline__ void wait_loads_but_one_tile() {
+  static_assert(2 * NIW < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NIW));
+}
+
 template <int D, int MASK, int NW, int BN, bool BUF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p) {
   using C = Cfg<D, NW, BN>;
   constexpr int NKB = C::NKB, NST = C::NST;
   constexpr int NKK = D / 16;  // MFMA k-steps for Q.K^T
   constexpr int NDB = D / 32;  // 32-row blocks of O^T
+  constexpr int S = D == 64 ? 3 : 2;  // LDS stages
   // one LDS object per buffer: the compiler then knows which buffer every global->LDS
   // load writes and waits only for those before reading a buffer
-  __shared__ __attribute__((aligned(1024))) char sk0[C::TILE], sk1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char sv0[C::TILE], sv1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char sk0[C::TILE], sk1[C::TILE], sk2[S == 3 ? C::TILE : 1];
+  __shared__ __attribute__((aligned(1024))) char sv0[C::TILE], sv1[C::TILE], sv2[S == 3 ? C::TILE : 1];
 
   if (p.unit_count && static_cast<int>(blockIdx.x) >= *p.unit_count) return;  // past this plan's units
   const int* u = p.units + static_cast<int64_t>(blockIdx.x) * 8;
@@ -272,26 +284,38 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     return fmaxf(mx, shfl_xor_f(mx, 32));
   };
 
-  // ---- prologue: tile 0 in LDS
+  // ---- prologue: tile 0 in LDS (and, with three stages, tile 1 on its way)
   if (ntiles > 0) {
     issue(PoolK{}, (lds_char*)sk0, 0);
     issue(PoolV{}, (lds_char*)sv0, 0);
   }
-  wait_all_loads();
+  if constexpr (S == 3) {
+    if (ntiles > 0) {
+      const int t1 = ntiles > 1 ? 1 : 0;  // a one-tile unit reloads tile 0: no load behind a branch
+      issue(PoolK{}, (lds_char*)sk1, t1);
+      issue(PoolV{}, (lds_char*)sv1, t1);
+      wait_loads_but_one_tile<C::NIW>();
+    } else {
+      wait_all_loads();
+    }
+  } else {
+    wait_all_loads();
+  }
   block_barrier();
 
-  // ---- step j: tile j is in buffer j % 2. Load tile j+1 into the other buffer (every
-  // wave is past tile j-1), compute tile j, then wait for this step's loads and meet at
-  // the barrier.
+  // ---- step j: tile j is in buffer j % S. Load tile j+S-1 into buffer (j+S-1) % S, the
+  // one tile j-1 used (every wave is past tile j-1), compute tile j, then wait for tile
+  // j+1 (with three stages the loads just issued stay in flight) and meet at the barrier.
   auto step = [&](auto par, int j) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    lds_char* kcur = (lds_char*)(P == 0 ? sk0 : sk1);
-    lds_char* vcur = (lds_char*)(P == 0 ? sv0 : sv1);
-    lds_char* knext = (lds_char*)(P == 0 ? sk1 : sk0);
-    lds_char* vnext = (lds_char*)(P == 0 ? sv1 : sv0);
-    // the last step reloads its own tile into the free buffer (an L2 hit that nothing
+    constexpr int N = (P + S - 1) % S;  // buffer of the tile loaded in this step
+    lds_char* kcur = (lds_char*)(P == 0 ? sk0 : P == 1 ? sk1 : sk2);
+    lds_char* vcur = (lds_char*)(P == 0 ? sv0 : P == 1 ? sv1 : sv2);
+    lds_char* knext = (lds_char*)(N == 0 ? sk0 : N == 1 ? sk1 : sk2);
+    lds_char* vnext = (lds_char*)(N == 0 ? sv0 : N == 1 ? sv1 : sv2);
+    // the last steps reload their own tile into the free buffer (an L2 hit that nothing
     // reads), so that no load sits behind a branch
-    const TileOffsets nxt = tile_offsets(j + 1 < ntiles ? j + 1 : j);
+    const TileOffsets nxt = tile_offsets(j + S - 1 < ntiles ? j + S - 1 : j);
     if (!wave_active) {
 #pragma unroll
       for (int i = 0; i < C::NIW; ++i) issue_one(PoolK{}, knext, nxt, i);
@@ -395,13 +419,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
         for (int db = 0; db < NDB; ++db)
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][st4], pb[st4], o[db], 0, 0, 0);
     }
-    wait_all_loads();
+    if constexpr (S == 3) wait_loads_but_one_tile<C::NIW>();
+    else wait_all_loads();
     block_barrier();
   };
-  for (int j = 0; j < ntiles; j += 2) {
+  for (int j = 0; j < ntiles; j += S) {
     step(std::integral_constant<int, 0>{}, j);
     if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
+    if constexpr (S == 3)
+      if (j + 2 < ntiles) step(std::integral_constant<int, 2>{}, j + 2);
   }
+  if constexpr (S == 3) wait_all_loads();  // no load may land in LDS after the workgroup ends
 
   // ---- finish: O / l and lse; accumulator i of block db holds dim 32db + 8(i/4) + 4half + i%4
   const float lt = lsum + shfl_xor_f(lsum, 32);

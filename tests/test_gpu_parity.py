@@ -100,6 +100,9 @@ SMALL = [
     ("mma_page4_d128_causal", [40, 130], [100, 131], 4, 2, 128, 4, 1, 0, "bf16"),
     ("mma_page64_d64", [33, 140], [500, 140], 2, 2, 64, 64, 1, 0, "bf16"),
     ("mma_page128_d128", [20, 9], [300, 129], 2, 2, 128, 128, 0, 0, "bf16"),
+    # tile units of 1 to 5 key tiles at head_dim 64, where the tile loads run two tiles ahead
+    ("mma_d64_tiles_1to5", [20] * 6, [1, 64, 65, 128, 192, 257], 2, 2, 64, 16, 0, 0, "bf16"),
+    ("mma_d64_causal_short", [20, 60, 130], [20, 130, 200], 2, 1, 64, 16, 1, 0, "bf16"),
     ("f32_all_masks_none", [1, 5, 2], [16, 40, 7], 2, 2, 16, 4, 0, 0, "f32"),
     ("f32_causal_gqa", [3, 1, 6], [7, 13, 6], 4, 1, 32, 3, 1, 0, "f32"),
     ("f32_block_d64", [10, 17], [10, 17], 2, 2, 64, 1, 2, 4, "f32"),

@@ -251,6 +251,24 @@ def context_source(w: Workload, seed: int = 0):
 
 # ---------------------------------------------------------------- the five workloads
 
+# Length draws, the first draws of each workload's generator (the page permutation and
+# the tensors follow from the same generator or from child streams).
+
+def ragged_prefill_query_lengths(rng: np.random.Generator) -> np.ndarray:
+    """32 query lengths, uniform integers in [1, 448]."""
+    return rng.integers(1, 448, 32, endpoint=True)
+
+
+def block_causal_span_lengths(rng: np.random.Generator) -> np.ndarray:
+    """64 span lengths, uniform integers in [256, 4096]."""
+    return rng.integers(256, 4096, 64, endpoint=True)
+
+
+def gqa_decode_context_lengths(rng: np.random.Generator) -> np.ndarray:
+    """256 context lengths, log-uniform in [512, 32768], rounded to the nearest integer."""
+    return np.rint(np.exp(rng.uniform(math.log(512), math.log(32768), 256))).astype(np.int64)
+
+
 def tiny_cross(seed: int = 0) -> Workload:
     """Tiny fp32 non-causal paged cross-attention: query lens [1,3], context [16,40],
     2 heads, head_dim 16, page_size 4, shuffled pages."""
@@ -268,7 +286,7 @@ def ragged_prefill(seed: int = 0) -> Workload:
     """Ragged prefill cross-attention: 32 requests, query lens U[1,448], context 1500,
     20 heads, head_dim 64, bf16, page_size 16, shuffled pages."""
     rng = np.random.default_rng(seed)
-    qo = rng.integers(1, 448, 32, endpoint=True)
+    qo = ragged_prefill_query_lengths(rng)
     return paged_case(qo, [1500] * 32, 20, 20, 64, 16, dtype="bf16", seed=seed, rng=rng,
                       name="ragged_prefill_cross")
 
@@ -277,7 +295,7 @@ def block_causal(seed: int = 0) -> Workload:
     """Cacheless ragged block-causal self-attention: 64 spans U[256,4096], block 64,
     16 heads, head_dim 128, bf16."""
     rng = np.random.default_rng(seed)
-    lens = rng.integers(256, 4096, 64, endpoint=True)
+    lens = block_causal_span_lengths(rng)
     return ragged_case(lens, 16, 128, dtype="bf16", mask_mode=MASK_BLOCK_CAUSAL, block_size=64,
                        seed=seed, name="block_causal_ragged")
 
@@ -286,7 +304,7 @@ def gqa_decode(seed: int = 0) -> Workload:
     """Causal GQA paged decode: 256 requests x 1 query, 32 q / 8 kv heads, head_dim 128,
     bf16, page_size 16, context lens log-uniform in [512, 32768], shuffled pages."""
     rng = np.random.default_rng(seed)
-    kv = np.rint(np.exp(rng.uniform(math.log(512), math.log(32768), 256))).astype(np.int64)
+    kv = gqa_decode_context_lengths(rng)
     return paged_case([1] * 256, kv, 32, 8, 128, 16, dtype="bf16", mask_mode=MASK_CAUSAL,
                       seed=seed, rng=rng, name="gqa_decode_causal")
 
@@ -297,7 +315,7 @@ def gqa_decode_tp8(seed: int = 0) -> Workload:
     holds num_heads / tp query heads and num_kv_heads / tp KV heads): 4 q heads and 1 KV
     head per rank, the same 256 contexts and pages."""
     rng = np.random.default_rng(seed)
-    kv = np.rint(np.exp(rng.uniform(math.log(512), math.log(32768), 256))).astype(np.int64)
+    kv = gqa_decode_context_lengths(rng)
     return paged_case([1] * 256, kv, 4, 1, 128, 16, dtype="bf16", mask_mode=MASK_CAUSAL,
                       seed=seed, rng=rng, name="gqa_decode_causal_tp8")
 

@@ -327,6 +327,53 @@ def pin_cacheless_slices(ref):
         assert np.allclose(lse[fin], bl[fin], atol=1e-12, rtol=0), w.name
 
 
+def _dispatch_cases():
+    """Workloads of each route of the oracle's workload entry point: cacheless spans under
+    every mask (an empty span among them), cacheless cross-attention between differently
+    sized query and key spans with empty spans on either side, and a shuffled paged table."""
+    return [synth.ragged_case([5, 9, 0, 1], 4, 8, num_kv_heads=2, dtype="bf16", mask_mode=NONE, seed=60),
+            synth.ragged_case([6, 1, 11, 0], 4, 8, num_kv_heads=1, dtype="bf16", mask_mode=CAUSAL, seed=61),
+            synth.ragged_case([7, 0, 12], 2, 8, dtype="f32", mask_mode=BLOCK, block_size=4, seed=62),
+            synth.ragged_cross_case([3, 0, 7, 2, 4], [9, 4, 0, 5, 1], 4, 8, num_kv_heads=2, dtype="bf16",
+                                    seed=63),
+            synth.paged_case([2, 0, 3, 1], [7, 5, 11, 0], 4, 2, 8, 3, dtype="f32", mask_mode=CAUSAL, seed=64)]
+
+
+def pin_run_workload(ref):
+    """The oracle's entry point over a workload (the one every GPU comparison calls)
+    equals scalar brute force that walks the workload's own page table token by token:
+    cacheless spans (identity table, page_size 1) under every mask, cross-attention whose
+    keys come from the second span set, and a paged table."""
+    for w in _dispatch_cases():
+        out, lse = ref.run_workload(w)
+        bo, bl = _brute(w)
+        assert out.shape == bo.shape, (w.name, out.shape, bo.shape)
+        assert np.allclose(out, bo, atol=1e-12, rtol=0), w.name
+        assert np.array_equal(np.isinf(lse), np.isinf(bl)), w.name
+        fin = np.isfinite(bl)
+        assert np.allclose(lse[fin], bl[fin], atol=1e-12, rtol=0), w.name
+
+
+def pin_workload_subsets(ref):
+    """A run restricted to some requests and heads reproduces exactly those rows and heads
+    of the full run and leaves every other entry NaN (the sampled comparisons rely on it)."""
+    for w in _dispatch_cases():
+        full_o, full_l = ref.run_workload(w)
+        nq, hq = full_l.shape
+        for reqs, heads in (([2, 0], sorted({hq - 1, hq // 2}, reverse=True)), ([w.batch_size - 1], None),
+                            (None, [0])):
+            so, sl = ref.run_workload(w, requests=reqs, heads=heads)
+            sel = np.zeros((nq, hq), bool)
+            rs = range(w.batch_size) if reqs is None else reqs
+            hs = list(range(hq)) if heads is None else heads
+            for r in rs:
+                for h in hs:
+                    sel[int(w.qo_indptr[r]):int(w.qo_indptr[r + 1]), h] = True
+            assert np.array_equal(so[sel], full_o[sel]), (w.name, reqs, heads)
+            assert np.array_equal(sl[sel], full_l[sel]), (w.name, reqs, heads)
+            assert np.isnan(so[~sel]).all() and np.isnan(sl[~sel]).all(), (w.name, reqs, heads)
+
+
 def _write_cases():
     """Shuffled pages with spare pages and partial last pages, an empty context, page
     sizes 1, 3 and 4, bf16 and fp32, and the identity table."""
@@ -364,4 +411,4 @@ def pin_context_write(ref):
 ALL_PINS = [pin_bf16_widening, pin_lengths, pin_uniform_scores, pin_single_key, pin_two_keys,
             pin_page_permutation, pin_gqa_repeat, pin_key_shift, pin_value_affine,
             pin_request_permutation, pin_split_merge, pin_library_sdpa, pin_brute_force,
-            pin_cacheless_slices, pin_context_write]
+            pin_cacheless_slices, pin_run_workload, pin_workload_subsets, pin_context_write]

@@ -26,6 +26,18 @@ def test_tiny_cross_golden():
 
 def test_generator_self_check():
     """Lengths of the seeded workloads: numpy 2.2 draws from default_rng(0) in the fixed order."""
+    rng = np.random.default_rng(0)
+    lens = synth.block_causal_span_lengths(rng)
+    assert int(lens.sum()) == 141675 and list(lens[:4]) == [3523, 2702, 2219, 1292]
+    rng = np.random.default_rng(0)
+    kv = synth.gqa_decode_context_lengths(rng)
+    assert int(kv.sum()) == 2321997 and list(kv[:4]) == [7240, 1572, 607, 548]
+    assert kv.min() >= 512 and kv.max() <= 32768
+    qo = synth.ragged_prefill_query_lengths(np.random.default_rng(0))
+    assert int(qo.sum()) == 7569 and list(qo[:4]) == [382, 286, 229, 121]
+    w2 = synth.whisper_decode(0)
+    assert list(set(w2.kv_lens())) == [1500] and int(w2.kv_indptr[-1]) == 6016
+    assert set(w2.kv_last_page_len) == {12} and w2.num_pages == 6016
     w3 = synth.ragged_prefill(0)
     assert int(w3.qo_indptr[-1]) == 7569 and list(w3.qo_lens()[:4]) == [382, 286, 229, 121]
     assert w3.k_pages.shape == (3008, 16, 20, 64)

@@ -10,7 +10,8 @@ import oracle.ref as ref
 from tests import oracle_pins
 
 _orig = {n: getattr(ref, n) for n in ("to_f64", "request_lengths", "gather_pages", "visible",
-                                      "attend", "merge_states", "ragged_attention", "write_context")}
+                                      "attend", "merge_states", "ragged_attention", "paged_attention",
+                                      "write_context", "run_workload")}
 
 
 def _gather_reversed_pages(pool, kv_indptr, kv_page_indices, r, kv_len, page_size, kv_head):
@@ -140,7 +141,52 @@ def _write_clears_tails(k_src, v_src, k_pages, v_pages, kv_indptr, kv_page_indic
     return kp, vp
 
 
+def _workload_drops_kv_spans(w, requests=None, heads=None):
+    """Routes cross-attention spans as self-attention: keys taken from the query spans."""
+    meta = dict(getattr(w, "meta", {}))
+    meta.pop("cu_seqlens_kv", None)
+    saved = w.meta
+    w.meta = meta
+    try:
+        return _orig["run_workload"](w, requests=requests, heads=heads)
+    finally:
+        w.meta = saved
+
+
+def _workload_cacheless_as_paged_rows(w, requests=None, heads=None):
+    """Takes the query spans' offsets for the key spans of cacheless workloads."""
+    if "cu_seqlens" not in getattr(w, "meta", {}):
+        return _orig["run_workload"](w, requests=requests, heads=heads)
+    return _orig["ragged_attention"](w.q, w.k_pages, w.v_pages, w.meta["cu_seqlens"], w.num_qo_heads,
+                                     w.num_kv_heads, dtype=w.dtype, mask_mode=w.mask_mode,
+                                     block_size=w.block_size, sm_scale=w.sm_scale, requests=requests,
+                                     heads=heads, cu_seqlens_kv=w.meta["cu_seqlens"])
+
+
+def _subset_rows_shifted(name):
+    """A subset run whose rows land one row off (the full run is untouched)."""
+    def f(*args, requests=None, heads=None, **kw):
+        out, lse = _orig[name](*args, requests=requests, heads=heads, **kw)
+        if requests is not None:
+            out, lse = np.roll(out, 1, axis=0), np.roll(lse, 1, axis=0)
+        return out, lse
+    return f
+
+
+def _subset_ignores_heads(name):
+    """A subset run that computes every head, not only the requested ones."""
+    def f(*args, requests=None, heads=None, **kw):
+        return _orig[name](*args, requests=requests, heads=None, **kw)
+    return f
+
+
 MUTATIONS = {
+    "workload_drops_kv_spans": ("run_workload", _workload_drops_kv_spans),
+    "workload_kv_spans_from_query_spans": ("run_workload", _workload_cacheless_as_paged_rows),
+    "paged_subset_rows_shifted": ("paged_attention", _subset_rows_shifted("paged_attention")),
+    "ragged_subset_rows_shifted": ("ragged_attention", _subset_rows_shifted("ragged_attention")),
+    "paged_subset_ignores_heads": ("paged_attention", _subset_ignores_heads("paged_attention")),
+    "ragged_subset_ignores_heads": ("ragged_attention", _subset_ignores_heads("ragged_attention")),
     "write_slot_from_page_index": ("write_context", _write_slot_from_page_index),
     "write_ignores_table": ("write_context", _write_ignores_table),
     "write_clears_tails": ("write_context", _write_clears_tails),

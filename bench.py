@@ -1,18 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the plan/run attention hot path on one MI355X.
 
-A step is one xattn_run over one batch of a seeded synthetic workload: every kernel
-of the run (attention, and the log-sum-exp merge when contexts are split). Plan is
-host work, done once before the timed region (its time is printed separately).
+A step is one xattn_run over one batch of a seeded synthetic workload: every kernel of
+the run (attention, and the log-sum-exp merge when contexts are split). Plan is host
+work, done once before the timed runs (its time is printed separately). Inputs are
+resident in HBM before any timed run.
 
-Default workload: Whisper-large-style decode cross-attention (64 requests x 1 query,
-context 1500, 20 heads, head_dim 64, bf16, page_size 16, shuffled pages), metric:
-effective KV GB/s = algorithmic K+V bytes (sum of kv_len x Hkv x D x 2 x 2 B) per
-step time. Prefill workloads report TFLOP/s = 4 x D x (visible query-key pairs x Hq)
-per step time.
+Headline workload (the largest of the five): causal GQA paged decode, 256 requests x 1
+query, 32 query / 8 KV heads, head_dim 128, bf16, page_size 16, contexts log-uniform in
+[512, 32768] (9.51 GB of K and V). Metric: effective KV GB/s = algorithmic K+V bytes
+(sum of kv_len x Hkv x D x 2 x 2 B) per step time. Prefill workloads report TFLOP/s =
+4 x D x (visible query-key pairs x Hq) per step time.
 
-Prints ONE JSON line. With --all, a "sweep" object carries the other workloads'
-numbers (same definitions) as well.
+`value` is the median over the timed runs, each run after 1 GiB is written to evict L2
+and the Infinity Cache (cold); the best run and back-to-back (warm) runs are reported
+beside it. The roofline object is the dominant kernel's algorithmic work over its own
+mean duration in the cold runs (HIP events the runtime stamps with the kernel's start
+and end, on the run's stream).
+
+Prints ONE JSON line. A "sweep" object carries the four other workloads, each with its
+own value, timing and roofline (--no-sweep: headline only; --all adds per-rank tensor-
+parallel shapes and the context write).
 """
 from __future__ import annotations
 
@@ -66,6 +74,35 @@ def warm_up(run, warmup):
         n += 5
         torch.cuda.synchronize()
     return n
+HEADLINE = "gqa_decode_causal"
+# what each workload is, by its sizes (the config objects of the JSON line)
+CONFIGS = {
+    "tiny_cross_f32": {"workload": "tiny_cross_f32", "requests": 2, "query_lens": [1, 3],
+                       "context_lens": [16, 40], "num_qo_heads": 2, "num_kv_heads": 2, "head_dim": 16,
+                       "page_size": 4, "mask": "none", "dtype": "f32"},
+    "whisper_decode_cross": {"workload": "whisper_decode_cross", "requests": 64, "query_tokens": 64,
+                             "context_len": 1500, "kv_tokens": 96000, "num_qo_heads": 20,
+                             "num_kv_heads": 20, "head_dim": 64, "page_size": 16, "mask": "none"},
+    "ragged_prefill_cross": {"workload": "ragged_prefill_cross", "requests": 32,
+                             "query_lens": "uniform 1-448 (sum 7569)", "context_len": 1500,
+                             "num_qo_heads": 20, "num_kv_heads": 20, "head_dim": 64, "page_size": 16,
+                             "mask": "none"},
+    "block_causal_ragged": {"workload": "block_causal_ragged", "spans": 64,
+                            "span_lens": "uniform 256-4096 (sum 141675)", "block_size": 64,
+                            "num_qo_heads": 16, "num_kv_heads": 16, "head_dim": 128,
+                            "page_table": "identity (cacheless)", "mask": "block_causal"},
+    "gqa_decode_causal": {"workload": "gqa_decode_causal", "requests": 256, "query_tokens": 256,
+                          "context_lens": "log-uniform 512-32768 (sum 2321997)", "num_qo_heads": 32,
+                          "num_kv_heads": 8, "head_dim": 128, "page_size": 16, "mask": "causal",
+                          "kv_bytes": 9510899712, "parallelism": "none (1 GPU)"},
+}
+DTYPE_NAME = {"bf16": "bf16", "f32": "f32"}
+
+
+def res_dtype(name):
+    return "f32" if name == "tiny_cross_f32" else "bf16"
+
+
 KERNEL_NAMES = {"decode": "attn_decode_kernel", "mfma": "attn_mma_kernel", "fp32": "attn_f32_kernel",
                 "merge": "merge_kernel"}
 
@@ -107,8 +144,29 @@ def to_dev(a, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 
-def measure(w, steps, warmup, dev, cold_steps=5):
-    """Plans, then times `steps` back-to-back runs (wall clock and per-kernel events)."""
+FLUSH_BYTES = 1 << 30  # written before each cold run: more than L2 and the 256 MB Infinity Cache
+
+
+def _stats(xs):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    return {"median_ms": round(float(np.median(xs)), 5), "best_ms": round(xs[0], 5),
+            "mean_ms": round(float(np.mean(xs)), 5), "runs": len(xs)}
+
+
+def measure(w, steps, warmup, dev, preroll_s=0.0):
+    """Plans w once, then times it two ways, each over `steps` runs:
+
+    * cold (the headline): before each run 1 GiB is written to evict L2 and the Infinity
+      Cache; the run's own duration comes from HIP events around it on its stream, and
+      each kernel's from events the runtime stamps with that kernel's start and end;
+    * warm: `steps` runs back to back (labelled warm), events between consecutive runs;
+      every TIMING_EVERY-th run carries the kernel events.
+
+    `warmup` untimed runs come first (None: as many as fill WARMUP_SECONDS), then, when
+    preroll_s > 0, cache flushes alone for that long (the GPU leaves its idle clocks only
+    under load; a flush is not a run)."""
     import torch
     import ragged_attention_serving_amd as xa
 
@@ -122,37 +180,52 @@ def measure(w, steps, warmup, dev, cold_steps=5):
               w.sm_scale, w.dtype)
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info()
-    warmed = warm_up(lambda: plan.run(q, k, v, out, lse), warmup)
+    run = lambda: plan.run(q, k, v, out, lse)  # noqa: E731
+    warmed = warm_up(run, warmup)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flushes = 0
+    if preroll_s > 0:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < preroll_s:
+            scratch.fill_(1.0)
+            flushes += 1
+            torch.cuda.synchronize()
 
-    # timed region: exactly `steps` runs, synchronised on both sides; on every TIMING_EVERY-th
-    # run the library launches each kernel with HIP events stamped with its start and end,
-    # on the run's stream, which give the per-kernel durations
-    plan.set_timing(TIMING_EVERY)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    # cold runs, one at a time
+    plan.set_timing(1)
+    cold, cold_k = [], {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(steps):
-        plan.run(q, k, v, out, lse)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    stages = plan.timing()
-    plan.set_timing(0)
-
-    # cold runs: 1 GiB written between runs to evict L2 and the Infinity Cache
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cold = []
-    for _ in range(cold_steps):
         scratch.fill_(1.0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        plan.run(q, k, v, out, lse)
+        run()
         e1.record()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
+        for st, (ms, n) in plan.timing().items():
+            if n:
+                cold_k.setdefault(st, []).append(ms / n)
     del scratch
+
+    # warm runs, back to back
+    plan.set_timing(TIMING_EVERY)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i].record()
+        run()
+    ev[steps].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / max(steps, 1)
+    warm = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    warm_k = {st: ms / n for st, (ms, n) in plan.timing().items() if n}
+    plan.set_timing(0)
     plan.close()
     del q, k, v, out, lse
-    return dict(plan_ms=plan_ms, wall_ms=wall_ms, stages=stages, info=info, warmup=warmed,
-                cold_ms=float(np.median(cold)) if cold else None)
+    return dict(plan_ms=plan_ms, info=info, warmup=warmed, preroll_flushes=flushes,
+                cold=cold, cold_kernel={st: float(np.mean(x)) for st, x in cold_k.items()},
+                warm=warm, warm_kernel=warm_k, warm_wall_ms=wall_ms)
 
 
 def measure_write(w, steps, warmup, dev):
@@ -185,35 +258,58 @@ def measure_write(w, steps, warmup, dev):
             "hbm_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-def summarize(w, m):
+def summarize(w, m, steps):
+    """One workload's entry: value from the cold runs (median), warm beside it, and the
+    roofline of the dominant kernel from its cold durations."""
     kv_bytes, flops, decode = workload_numbers(w, m["info"])
-    per = {}
-    for st, (ms, n) in m["stages"].items():
-        if n:
-            per[st] = ms / n
+    per = m["cold_kernel"]
     dominant = max(per, key=per.get) if per else None
-    res = dict(workload=w.name, decode=decode, kv_bytes=kv_bytes, flops=flops, plan_ms=round(m["plan_ms"], 3),
-               ms_per_step=m["wall_ms"], cold_ms_per_step=m["cold_ms"],
-               kernel_ms={k: round(v, 5) for k, v in per.items()}, dominant=dominant,
-               schedule=m["info"])
+    cold, warm = _stats(m["cold"]), _stats(m["warm"])
     if decode:
-        res["GBps"] = kv_bytes / (m["wall_ms"] * 1e-3) / 1e9
-        res["GBps_cold"] = kv_bytes / (m["cold_ms"] * 1e-3) / 1e9 if m["cold_ms"] else None
-        res["kernel_GBps"] = kv_bytes / (per[dominant] * 1e-3) / 1e9 if dominant else None
-        res["hbm_frac"] = res["kernel_GBps"] / HBM_PEAK_GBS if dominant else None
+        work, unit, scale = kv_bytes, "GB/s", 1e9
+        bound, peak, runit = "hbm", HBM_PEAK_GBS, "GB/s"
+    elif w.dtype == "bf16":
+        work, unit, scale = flops, "TFLOP/s", 1e12
+        bound, peak, runit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
-        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
-        res["TFLOPs"] = flops / (m["wall_ms"] * 1e-3) / 1e12
-        res["TFLOPs_cold"] = flops / (m["cold_ms"] * 1e-3) / 1e12 if m["cold_ms"] else None
-        res["kernel_TFLOPs"] = flops / (per[dominant] * 1e-3) / 1e12 if dominant else None
-        res["mfma_frac"] = res["kernel_TFLOPs"] / peak if dominant else None
+        work, unit, scale = flops, "TFLOP/s", 1e12
+        bound, peak, runit = "alu", F32_PEAK_TFLOPS, "TFLOP/s"
+    rate = lambda ms: work / (ms * 1e-3) / scale if ms else None  # noqa: E731
+    res = {
+        "workload": w.name, "value": round(rate(cold["median_ms"]), 3), "unit": unit,
+        "ms_per_step": cold["median_ms"],
+        "value_best": round(rate(cold["best_ms"]), 3),
+        "value_warm": round(rate(warm["median_ms"]), 3),
+        "timing": {"cold": cold, "warm": warm, "warm_wall_ms_per_step": round(m["warm_wall_ms"], 5),
+                   "cold_protocol": "each run after writing 1 GiB (L2 and Infinity Cache evicted); "
+                                    "HIP events around the run on its stream"},
+        "work": {"kv_bytes": kv_bytes, "flops": flops, "visible_pairs": int(m["info"]["visible_pairs"])},
+        "kernel_ms_cold": {k: round(v, 5) for k, v in per.items()},
+        "kernel_ms_warm": {k: round(v, 5) for k, v in m["warm_kernel"].items()},
+        "plan_ms": round(m["plan_ms"], 3), "warmup": m["warmup"], "schedule": m["info"],
+    }
+    if dominant:
+        kms = per[dominant]
+        achieved = rate(kms)
+        wk = m["warm_kernel"].get(dominant)
+        res["roofline"] = {
+            "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": runit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dominant, w.name),
+            "kernel": KERNEL_NAMES[dominant], "kernel_ms": round(kms, 5),
+            "kernel_timing": f"cold: mean of the kernel's own duration over {len(m['cold'])} runs, "
+                             "each after a 1 GiB write",
+            "kernel_ms_warm": round(wk, 5) if wk else None,
+            "frac_warm": round(rate(wk) / peak, 4) if wk else None,
+            "kernel_source_sha": source_sha(dominant),
+        }
+    if not decode and w.dtype == "bf16" and dominant:
         # compulsory HBM bytes of a prefill: K and V once, Q read and out and lse written once
-        elt = 2 if w.dtype == "bf16" else 4
+        elt = 2
         rows = int(w.qo_lens().sum()) * w.num_qo_heads
         hbm_bytes = kv_bytes + rows * (2 * w.head_dim * elt + 4)
-        res["hbm_bytes_compulsory"] = hbm_bytes
-        res["hbm_GBps_compulsory"] = hbm_bytes / (per[dominant] * 1e-3) / 1e9 if dominant else None
-        res["hbm_frac_compulsory"] = res["hbm_GBps_compulsory"] / HBM_PEAK_GBS if dominant else None
+        res["hbm_compulsory"] = {"bytes": hbm_bytes,
+                                 "GBps": round(hbm_bytes / (per[dominant] * 1e-3) / 1e9, 1),
+                                 "frac": round(hbm_bytes / (per[dominant] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     return res
 
 
@@ -244,19 +340,39 @@ def _cpu_worker(args):
         ctx = None
     from oracle import ref
     w = _CPU_W
-    elt = 2 if w.dtype == "bf16" else 4
-    kv = w.kv_lens()
-    done_bytes, done_req, i = 0, 0, start
+    work = _request_work(w)
+    done_work, done_req, i = 0, 0, start
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < wall_s:
         r = i % w.batch_size
         ref.run_workload(w, requests=[r])
-        done_bytes += int(kv[r]) * w.num_kv_heads * w.head_dim * 2 * elt
+        done_work += int(work[r])
         done_req += 1
         i += step
     el = time.perf_counter() - t0
     del ctx  # (the limit only needs to hold while this worker runs)
-    return done_bytes, done_req, el
+    return done_work, done_req, el
+
+
+def _request_work(w):
+    """Per request, the metric's algorithmic work: K+V bytes for a decode workload, visible
+    pair FLOPs (4 x D per pair and query head) otherwise."""
+    elt = 2 if w.dtype == "bf16" else 4
+    g = w.num_qo_heads // w.num_kv_heads
+    if bool(np.all(w.qo_lens() * g <= 8)) and w.dtype == "bf16":
+        return w.kv_lens() * w.num_kv_heads * w.head_dim * 2 * elt
+    qo, kv = w.qo_lens(), w.kv_lens()
+    pairs = np.zeros(w.batch_size, np.int64)
+    for r in range(w.batch_size):
+        p = kv[r] - qo[r] + np.arange(qo[r])
+        if w.mask_mode == 0:
+            vis = np.full(qo[r], kv[r])
+        elif w.mask_mode == 1:
+            vis = np.minimum(p + 1, kv[r])
+        else:
+            vis = np.minimum((p // w.block_size + 1) * w.block_size, kv[r])
+        pairs[r] = int(vis.sum())
+    return pairs * 4 * w.head_dim * w.num_qo_heads
 
 
 def cpu_baseline(w, cpu_seconds=24.0):
@@ -274,29 +390,40 @@ def cpu_baseline(w, cpu_seconds=24.0):
         t0 = time.perf_counter()
         parts = pool.map(_cpu_worker, [(k, n, wall) for k in range(n)])
         el = time.perf_counter() - t0
-    done_bytes = sum(p[0] for p in parts)
+    done_work = sum(p[0] for p in parts)
     done_req = sum(p[1] for p in parts)
-    elt = 2 if w.dtype == "bf16" else 4
-    kv_bytes = int(w.kv_lens().sum()) * w.num_kv_heads * w.head_dim * 2 * elt
-    return {"value": done_bytes / el / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+    work = _request_work(w)
+    decode = bool(np.all(w.qo_lens() * (w.num_qo_heads // w.num_kv_heads) <= 8)) and w.dtype == "bf16"
+    scale, unit = (1e9, "GB/s") if decode else (1e12, "TFLOP/s")
+    return {"value": done_work / el / scale, "unit": unit, "cores": n, "kind": "oracle",
+            "host_cores": host_cores(),
             "sample": f"{done_req} request passes (all {w.num_qo_heads} heads each, {done_req / w.batch_size:.2f} "
-                      f"x the workload's {w.batch_size} requests) by {n} processes in {el:.1f} s",
-            "workload_bytes": kv_bytes}
+                      f"x the workload's {w.batch_size} requests, taken in turn) by {n} processes in {el:.1f} s",
+            "workload_work": int(work.sum())}
+
+
+def host_cores():
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    return {"affinity": aff, "cpu_count": os.cpu_count()}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=30,
+                    help="timed runs per workload, cold (after a 1 GiB flush each) and again warm")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed runs before the timed ones (default: as many as fill %.1f s)" % WARMUP_SECONDS)
-    ap.add_argument("--workload", default="whisper_decode_cross")
-    ap.add_argument("--all", action="store_true", help="also measure every other workload")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-sweep", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--all", action="store_true",
+                    help="also measure the per-rank tensor-parallel shapes and the context write")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=24.0,
                     help="CPU seconds (summed over the worker processes) for the oracle baseline")
-    ap.add_argument("--cold-steps", type=int, default=5,
-                    help="runs timed one by one after a 1 GiB cache flush (0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device once (the known-size kernel that scales "
                          "the FETCH_SIZE and WRITE_SIZE counters) and exit")
@@ -312,15 +439,9 @@ def main():
     import torch
     from ragged_attention_serving_amd import synth
 
-    cpu_line = None
-    if not (args.no_cpu_baseline or args.copy_calibration or args.context_write):
-        # before anything touches the GPU: the oracle's worker processes are forked
-        log(f"[bench] timing the CPU oracle on {args.workload}")
-        cpu_line = cpu_baseline({**synth.WORKLOADS, **synth.TP_WORKLOADS}[args.workload](0), args.cpu_seconds)
-        log(f"[bench] cpu baseline {json.dumps(cpu_line)}")
-
-    dev = torch.device("cuda:0")
+    all_workloads = {**synth.WORKLOADS, **synth.TP_WORKLOADS}
     if args.copy_calibration:
+        dev = torch.device("cuda:0")
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -328,83 +449,65 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel() * 4}), flush=True)
         return
-    all_workloads = {**synth.WORKLOADS, **synth.TP_WORKLOADS}
     log(f"[bench] generating {args.workload}")
     w = all_workloads[args.workload](0)
+    cpu_line = None
+    if not (args.no_cpu_baseline or args.context_write):
+        # before anything touches the GPU: the oracle's worker processes are forked
+        log(f"[bench] timing the CPU oracle on {args.workload}")
+        cpu_line = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] cpu baseline {json.dumps(cpu_line)}")
+    dev = torch.device("cuda:0")
     if args.context_write:
         print(json.dumps(measure_write(w, args.steps, args.warmup, dev)), flush=True)
         return
     log(f"[bench] measuring {args.workload}: steps={args.steps} warmup={args.warmup}")
-    m = measure(w, args.steps, args.warmup, dev, args.cold_steps)
-    res = summarize(w, m)
+    # the headline is measured first in the process: after its `warmup` runs, 0.3 s of
+    # cache flushes alone bring the GPU out of its idle clocks before the timed runs
+    m = measure(w, args.steps, args.warmup, dev, preroll_s=0.3)
+    res = summarize(w, m, args.steps)
     log(f"[bench] {json.dumps({k: v for k, v in res.items() if k != 'schedule'})}")
-
-    st = res["dominant"]
-    per_ms = res["kernel_ms"][st]
-    if res["decode"]:
-        achieved = res["kv_bytes"] / (per_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        value = res["kv_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
-        unit = "GB/s"
-    else:
-        achieved = res["flops"] / (per_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-        value = res["flops"] / (res["ms_per_step"] * 1e-3) / 1e12
-        unit = "TFLOP/s"
-    roof["traffic"] = traffic_for(st, w.name)
-    roof["kernel"] = KERNEL_NAMES[st]
-    roof["kernel_ms"] = round(per_ms, 5)
-    roof["kernel_source_sha"] = source_sha(st)
+    del w, m
+    torch.cuda.empty_cache()
 
     line = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": m["warmup"], "ms_per_step": round(res["ms_per_step"], 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "requests": w.batch_size, "query_tokens": int(w.qo_indptr[-1]),
-                   "kv_tokens": int(w.kv_lens().sum()), "num_qo_heads": w.num_qo_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
-                   "mask_mode": w.mask_mode, "block_size": w.block_size, "parallelism": "none (1 GPU)"},
-        "roofline": roof,
-        "cold_ms_per_step": round(res["cold_ms_per_step"], 5) if res["cold_ms_per_step"] else None,
-        "plan_ms": res["plan_ms"],
-        "schedule": res["schedule"],
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": res["warmup"], "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[res_dtype(args.workload)],
+        "data": "synthetic",
+        "config": CONFIGS[args.workload] if args.workload in CONFIGS else {"workload": args.workload},
+        "roofline": res.get("roofline"),
+        "value_best": res["value_best"], "value_warm": res["value_warm"],
+        "timing": res["timing"], "kernel_ms_cold": res["kernel_ms_cold"],
+        "kernel_ms_warm": res["kernel_ms_warm"], "plan_ms": res["plan_ms"], "schedule": res["schedule"],
+        "work": res["work"],
     }
+    if "hbm_compulsory" in res:
+        line["hbm_compulsory"] = res["hbm_compulsory"]
     if cpu_line is not None:
         line["cpu_baseline"] = cpu_line
-    if args.all:
+    if not args.no_sweep:
+        names = [n for n in synth.WORKLOADS if n != args.workload]
+        if args.all:
+            names += [n for n in synth.TP_WORKLOADS if n != args.workload]
         sweep = {}
-        for name, fn in synth.WORKLOADS.items():
-            if name == w.name:
-                continue
+        for name in names:
             log(f"[bench] sweep: generating {name}")
-            ws = fn(0)
+            ws = all_workloads[name](0)
             log(f"[bench] sweep: measuring {name}")
             ms = measure(ws, args.steps, None, dev)
-            r = summarize(ws, ms)
+            r = summarize(ws, ms, args.steps)
             r.pop("schedule", None)
-            r["warmup"] = ms["warmup"]
+            r["config"] = CONFIGS.get(name, {"workload": name})
             sweep[name] = r
             log(f"[bench] {json.dumps(r)}")
             del ws, ms
             torch.cuda.empty_cache()
-        for name, fn in synth.TP_WORKLOADS.items():
-            log(f"[bench] sweep: generating {name}")
-            ws = fn(0)
-            log(f"[bench] sweep: measuring {name}")
-            ms = measure(ws, args.steps, None, dev)
-            r = summarize(ws, ms)
-            r.pop("schedule", None)
-            r["warmup"] = ms["warmup"]
-            sweep[name] = r
-            log(f"[bench] {json.dumps(r)}")
-            del ws, ms
-            torch.cuda.empty_cache()
-        log("[bench] sweep: context write")
-        wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), args.steps, None, dev)
-        sweep[wr["workload"]] = wr
-        log(f"[bench] {json.dumps(wr)}")
+        if args.all:
+            log("[bench] sweep: context write")
+            wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), args.steps, None, dev)
+            sweep[wr["workload"]] = wr
+            log(f"[bench] {json.dumps(wr)}")
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)
 

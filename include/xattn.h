@@ -86,6 +86,20 @@ enum xattn_status {
  * units (splitting long contexts into KV chunks whose partial results are merged
  * on the log-sum-exp), and stage the schedule for xattn_run.
  *
+ * Page "mstar.engine.resources.attn.cross", FlashInferCrossManager.plan: one step's
+ * query packing (QueryPacking: requests in packed order and cumulative query lengths)
+ * becomes an immutable, opaque planned object that every layer's run of the step
+ * reuses; FlashInferCrossManager.force_double_buffer: its host staging and non-blocking
+ * copy are kept per slot, two slots, so a plan never overwrites what an earlier run
+ * still reads.
+ *
+ * The argument list is the page table and packing of the problem statement
+ * (qo_indptr, kv_indptr, kv_page_indices, kv_last_page_len, head counts, head_dim,
+ * page_size, mask) plus what a C call cannot infer: batch_size, block_size, sm_scale,
+ * dtype, stream, and one deliberate addition, num_pages, the size of the K and V
+ * pools, so that every page index is checked against the pool before any kernel
+ * reads through it (without it a bad index could only be caught by a device fault).
+ *
  * plan            in/out. *plan == NULL creates a handle; otherwise the new schedule
  *                 is written into the handle's other slot (two slots: pinned host
  *                 staging + device copy + fp32 split workspace each). Before a slot is
@@ -150,6 +164,11 @@ XATTN_API int xattn_plan_create(xattn_plan_t* plan, int32_t flags);
  * attention kernels, and the log-sum-exp merge kernel when a context was split, on
  * `stream`, then records the slot's fence there. Any number of runs (one per layer,
  * each with its own q/k/v/out) may share one plan.
+ * When the schedule splits contexts (xattn_plan_info: num_merge_rows > 0) its runs share
+ * the slot's fp32 workspace of partial results. A run on another stream than the latest
+ * run that used it therefore first waits for that stream (an event recorded there), so
+ * runs of a split schedule on several streams execute one after another and never mix
+ * their partials; runs on one stream are ordered by the stream and record nothing.
  *
  * q, k_pages, v_pages  device pointers, layouts above, 16-byte aligned; k_pages and
  *                      v_pages are not written.
@@ -203,13 +222,17 @@ XATTN_API int xattn_write_kv(xattn_plan_t plan, const void* k_src, const void* v
                              void* v_pages, void* stream);
 
 /* 1 if the next xattn_plan on this handle (on the same stream) would not wait, 0 if it
- * would, negative on error. Never blocks. */
+ * would, negative on error. Never blocks. Page "mstar.engine.resources.attn.cross",
+ * force_double_buffer: the host runs ahead of the device, and this tells it whether the
+ * slot the next plan fills is still in use. */
 XATTN_API int xattn_plan_ready(xattn_plan_t plan);
 
-/* Waits on both slot fences, then frees the handle. NULL is ignored. */
+/* Waits on both slot fences, then frees the handle. NULL is ignored.
+ * Plumbing of the C boundary (a handle's lifetime); no page passage defines it. */
 XATTN_API void xattn_plan_destroy(xattn_plan_t plan);
 
-/* Thread-local message for the last non-OK status of this thread ("" if none). */
+/* Thread-local message for the last non-OK status of this thread ("" if none).
+ * Plumbing of the C boundary (error reporting); no page passage defines it. */
 XATTN_API const char* xattn_last_error(void);
 
 /* What a schedule holds (host-side summary, no GPU involved). */
@@ -236,6 +259,8 @@ typedef struct xattn_schedule_info {
  * kv_head * group + row % group. When `merges` is not NULL it receives num_merge_rows
  * records of 4 int32: {out_row = token * num_qo_heads + head, first workspace row,
  * chunk count, workspace row stride between chunks}. Same errors as xattn_plan.
+ * Inspection of the plan step (page "mstar.engine.resources.attn.cross",
+ * FlashInferCrossManager.plan) without a device; the pages define no such call.
  */
 XATTN_API int xattn_schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
                    const int32_t* kv_page_indices, const int32_t* kv_last_page_len,
@@ -244,7 +269,9 @@ XATTN_API int xattn_schedule(const int32_t* qo_indptr, const int32_t* kv_indptr,
                    int32_t block_size, int32_t dtype, int32_t force_chunk,
                    xattn_schedule_info* info, int32_t* units, int32_t* merges);
 
-/* The summary of the handle's current schedule. */
+/* The summary of the handle's current schedule. Inspection of the opaque plan result
+ * (page "mstar.engine.resources.attn.cross", FlashInferCrossManager.plan); the pages
+ * define no such call. */
 XATTN_API int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info);
 
 /*
@@ -256,6 +283,7 @@ XATTN_API int xattn_plan_info(xattn_plan_t plan, xattn_schedule_info* info);
  * xattn_plan_timing waits for the recorded events, writes the summed milliseconds
  * and the launch count per stage {0 fp32, 1 bf16 decode, 2 bf16 MFMA tile, 3 merge}
  * into ms[4] and launches[4], and clears the records. every <= 0 stops recording.
+ * Measurement plumbing; no page passage defines it (the pages publish no timings).
  */
 XATTN_API int xattn_plan_set_timing(xattn_plan_t plan, int every);
 XATTN_API int xattn_plan_timing(xattn_plan_t plan, double* ms, int32_t* launches);

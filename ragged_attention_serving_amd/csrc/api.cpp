@@ -14,6 +14,8 @@
 //    ordered before the new copy. Runs on the plan's own stream are: the new copy is
 //    queued behind them. A run on another stream records the slot's fence, and a plan
 //    on another stream than the one the slot last used drains that stream first.
+// Runs of one slot whose schedule splits contexts share the slot's fp32 workspace, so a
+// run on another stream than the latest such run first waits for that stream.
 // So the common case, plan and runs on one stream, records nothing per run.
 #include <hip/hip_runtime.h>
 
@@ -66,6 +68,11 @@ struct Slot {
   // runs on streams other than the plan's: one event per stream, after its latest run
   std::vector<std::pair<void*, hipEvent_t>> foreign;
   size_t foreign_live = 0;        // entries recorded since the slot was last planned
+  // the split workspace is one buffer per slot: the stream of the latest run that used
+  // it since the slot was planned, and an event a run on another stream waits on
+  void* ws_stream = nullptr;
+  bool ws_used = false;
+  hipEvent_t ws_event = nullptr;
   bool ready = false;
   // schedule summary and device offsets (in int32 words from dev)
   Schedule sched;
@@ -248,6 +255,8 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
       return fail(hip_err(e, "hipEventCreate"));
     if ((e = hipEventCreateWithFlags(&sl.uploaded, hipEventDisableTiming)) != hipSuccess)
       return fail(hip_err(e, "hipEventCreate"));
+    if ((e = hipEventCreateWithFlags(&sl.ws_event, hipEventDisableTiming)) != hipSuccess)
+      return fail(hip_err(e, "hipEventCreate"));
   }
   if (sl.uploaded_rec) {
     // the previous copy out of the pinned buffer must be done before it is rewritten
@@ -264,6 +273,9 @@ int xattn_plan(xattn_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_i
     if ((e = hipEventSynchronize(sl.foreign[i].second)) != hipSuccess) return fail(hip_err(e, "hipEventSynchronize"));
   }
   sl.foreign_live = 0;
+  // every run that used the workspace is done or ordered before this plan's copy, which
+  // every later run of the slot follows
+  sl.ws_used = false;
 
   // device image (int32 words): header | reqs | units per family | merges | page indices |
   // kv starts. The header holds each family's unit count and the merge count, which the
@@ -414,14 +426,33 @@ hipError_t slot_mark(Slot& sl, void* stream) {
   return hipEventRecord(sl.foreign[i].second, static_cast<hipStream_t>(stream));
 }
 
+// Runs of a split schedule share the slot's workspace (partial rows, then the merge that
+// reads them): a run on another stream than the latest run that used it waits for that
+// stream, so such runs execute one after another. Runs on one stream are ordered anyway,
+// and record nothing.
+hipError_t ws_order(Slot& sl, void* stream) {
+  if (sl.ws_used && sl.ws_stream != stream) {
+    hipError_t e = hipEventRecord(sl.ws_event, static_cast<hipStream_t>(sl.ws_stream));
+    if (e == hipSuccess) e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), sl.ws_event, 0);
+    if (e != hipSuccess) return e;
+  }
+  sl.ws_used = true;
+  sl.ws_stream = stream;
+  return hipSuccess;
+}
+
 }  // namespace
 
-int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages, void* out,
-              float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the run entry points.
+int check_run_args(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+                   void* out, float* lse) {
   if (!plan || plan->cur < 0 || !plan->slot[plan->cur].ready)
     return set_err(XATTN_ERR_INVALID_ARG, "run without a successful plan");
-  Slot& sl = plan->slot[plan->cur];
-  const Schedule& s = sl.sched;
+  const Schedule& s = plan->slot[plan->cur].sched;
   size_t nunits = 0;
   for (int f = 0; f < xattn::FAM_COUNT; ++f) nunits += s.units[f].size();
   if (nunits > 0 && (!q || !out)) return set_err(XATTN_ERR_INVALID_ARG, "q and out are required");
@@ -431,10 +462,19 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
                         reinterpret_cast<uintptr_t>(v_pages) | reinterpret_cast<uintptr_t>(out);
   if (mis & 15) return set_err(XATTN_ERR_INVALID_ARG, "q, k_pages, v_pages and out must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(lse) & 3) return set_err(XATTN_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  return XATTN_OK;
+}
 
+// Launches the current slot's attention kernels, and the merge when contexts were split,
+// on `stream`, with the split workspace at ws_o ([rows][d]) and ws_lse ([rows]).
+// `timing` allows the per-kernel events of xattn_plan_set_timing.
+int launch_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages, void* out,
+               float* lse, void* stream, float* ws_o, float* ws_lse, bool timing) {
+  Slot& sl = plan->slot[plan->cur];
+  const Schedule& s = sl.sched;
   hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if ((e = slot_wait(sl, stream)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+  const bool stable = (plan->flags & XATTN_PLAN_GRAPH_STABLE) != 0;
 
   const int32_t* dev = static_cast<const int32_t*>(sl.dev);
   AttnParams p{};
@@ -443,9 +483,8 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   p.v = v_pages;
   p.out = out;
   p.lse = lse;
-  const bool stable = (plan->flags & XATTN_PLAN_GRAPH_STABLE) != 0;
-  p.ws_o = sl.ws;
-  p.ws_lse = sl.ws ? sl.ws + static_cast<size_t>(sl.cap_ws_rows) * sl.d : nullptr;
+  p.ws_o = ws_o;
+  p.ws_lse = ws_lse;
   p.reqs = dev + sl.off_reqs;
   p.pages = s.identity ? nullptr : dev + sl.off_pages;
   p.merges = dev + sl.off_merges;
@@ -469,7 +508,7 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   p.pool_bytes = sl.pool_bytes;
 
   // optional per-kernel events (xattn_plan_set_timing)
-  const bool timed = plan->timing_every > 0 && plan->runs++ % plan->timing_every == 0 &&
+  const bool timed = timing && plan->timing_every > 0 && plan->runs++ % plan->timing_every == 0 &&
                      plan->timing_recs.size() < kMaxTimingRecs;
   auto event = [&](hipEvent_t* ev) -> hipError_t {
     if (!plan->event_pool.empty()) {
@@ -521,6 +560,27 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
     if ((e = xattn::launch_merge(p, sl.dtype, l)) != hipSuccess) return unused(l), hip_err(e, "merge kernel launch");
     launched(3, l);
   }
+  return XATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages, void* out,
+              float* lse, void* stream) {
+  int rc = check_run_args(plan, q, k_pages, v_pages, out, lse);
+  if (rc != XATTN_OK) return rc;
+  Slot& sl = plan->slot[plan->cur];
+  const Schedule& s = sl.sched;
+  hipError_t e;
+  if ((e = slot_wait(sl, stream)) != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+  const bool stable = (plan->flags & XATTN_PLAN_GRAPH_STABLE) != 0;
+  if ((stable ? sl.run_merge : !s.merges.empty()) && (e = ws_order(sl, stream)) != hipSuccess)
+    return hip_err(e, "workspace order");
+  float* ws_lse = sl.ws ? sl.ws + static_cast<size_t>(sl.cap_ws_rows) * sl.d : nullptr;
+  if ((rc = launch_run(plan, q, k_pages, v_pages, out, lse, stream, sl.ws, ws_lse, true)) != XATTN_OK)
+    return rc;
   if ((e = slot_mark(sl, stream)) != hipSuccess) return hip_err(e, "hipEventRecord");
   return XATTN_OK;
 }
@@ -642,8 +702,12 @@ void xattn_plan_destroy(xattn_plan_t plan) {
       (void)hipEventSynchronize(sl.fence);
     for (size_t i = 0; i < sl.foreign_live; ++i) (void)hipEventSynchronize(sl.foreign[i].second);
     for (auto& f : sl.foreign) (void)hipEventDestroy(f.second);
+    if (sl.ws_used && sl.ws_event &&
+        hipEventRecord(sl.ws_event, static_cast<hipStream_t>(sl.ws_stream)) == hipSuccess)
+      (void)hipEventSynchronize(sl.ws_event);
     if (sl.fence) (void)hipEventDestroy(sl.fence);
     if (sl.uploaded) (void)hipEventDestroy(sl.uploaded);
+    if (sl.ws_event) (void)hipEventDestroy(sl.ws_event);
     if (sl.host) (void)hipHostFree(sl.host);
     if (sl.dev) (void)hipFree(sl.dev);
     if (sl.ws) (void)hipFree(sl.ws);

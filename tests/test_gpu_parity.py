@@ -1,17 +1,20 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element.
 
 Tolerances: bf16 inputs max |out error| <= 2e-2, fp32 inputs <= 1e-5; lse <= 1e-3.
-The seeded workloads at full size are compared on whole outputs where the oracle is
-quick (tiny, Whisper decode, ragged prefill) and on sampled requests and heads where
-it is not (block-causal spans, GQA decode); small cases cover every kernel family,
-mask, head grouping, page size, split and edge case.
+The seeded workloads are compared at full size on every output row and head (the
+block-causal spans and the GQA decode with the oracle computed request by request on
+host threads); small cases cover every kernel family, mask, head grouping, page size,
+split and edge case.
 """
+import time
+
 import numpy as np
 import pytest
 
 from oracle import ref
 from ragged_attention_serving_amd import synth
 from tests.gpu_util import compare, log, run_gpu, to_device
+from tests.oracle_threads import oracle_by_request
 
 pytestmark = pytest.mark.gpu
 
@@ -38,44 +41,35 @@ def test_ragged_prefill(gpu):
     _full(synth.ragged_prefill(0), gpu)
 
 
-def test_block_causal_sampled(gpu):
-    w = synth.block_causal(0)
-    log(f"[parity] {w.name} (sampled spans x heads)")
+def _full_by_request(w, gpu):
+    """The whole workload on the GPU against the oracle over every request and head, the
+    oracle computed request by request on a pool of host threads."""
+    log(f"[parity] {w.name} (every request and head)")
     out, lse, plan = run_gpu(w, gpu)
     log(f"  schedule {plan.info()}")
-    lens = w.qo_lens()
-    spans = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 5, 37})
-    heads = [0, 7, 15]
-    ro, rl = ref.run_workload(w, requests=spans, heads=heads)
-    rows = np.concatenate([np.arange(w.qo_indptr[s], w.qo_indptr[s + 1]) for s in spans])
-    compare(out[rows][:, heads], lse[rows][:, heads], ro[rows][:, heads], rl[rows][:, heads],
-            w.dtype, label=f"{w.name} spans {spans} heads {heads}")
-    assert np.isfinite(lse).all() and not np.isnan(out).any()
+    plan.close()
+    t0 = time.perf_counter()
+    ro, rl = oracle_by_request(w)
+    log(f"  oracle over {w.batch_size} requests in {time.perf_counter() - t0:.1f} s")
+    compare(out, lse, ro, rl, w.dtype, label=w.name)
+    return out, lse
+
+
+def test_block_causal_full(gpu):
+    """Block-causal spans of 256-4096 tokens at full size: every span, every head."""
+    _full_by_request(synth.block_causal(0), gpu)
 
 
 def test_tensor_parallel_rank_shapes(gpu):
     """One rank's heads of the decode workloads under tensor parallelism over heads."""
-    w = synth.whisper_decode_tp4(0)
-    _full(w, gpu)
-    w = synth.gqa_decode_tp8(0)
-    log(f"[parity] {w.name} (sampled requests)")
-    out, lse, plan = run_gpu(w, gpu)
-    kv = w.kv_lens()
-    reqs = sorted({int(np.argmax(kv)), int(np.argmin(kv)), 0, 77, 255})
-    ro, rl = ref.run_workload(w, requests=reqs)
-    compare(out[reqs], lse[reqs], ro[reqs], rl[reqs], w.dtype, label=f"{w.name} requests {reqs}")
+    _full(synth.whisper_decode_tp4(0), gpu)
+    _full_by_request(synth.gqa_decode_tp8(0), gpu)
 
 
-def test_gqa_decode_sampled(gpu):
-    w = synth.gqa_decode(0)
-    log(f"[parity] {w.name} (sampled requests)")
-    out, lse, plan = run_gpu(w, gpu)
-    log(f"  schedule {plan.info()}")
-    kv = w.kv_lens()
-    reqs = sorted({int(np.argmax(kv)), int(np.argmin(kv)), 0, 100, 255})
-    ro, rl = ref.run_workload(w, requests=reqs)
-    compare(out[reqs], lse[reqs], ro[reqs], rl[reqs], w.dtype, label=f"{w.name} requests {reqs}")
-    assert np.isfinite(lse).all() and not np.isnan(out).any()
+def test_gqa_decode_full(gpu):
+    """The GQA decode at full size (9.5 GB of K and V, split contexts merged): every
+    request, every head."""
+    _full_by_request(synth.gqa_decode(0), gpu)
 
 
 # ------------------------------------------------------------------ small cases
@@ -302,40 +296,53 @@ def test_tile_kernel_variants(rows, gpu, monkeypatch):
 
 
 def test_runs_and_plans_on_several_streams(gpu):
-    """Runs on streams other than the plan's, and a plan that moves to another stream,
-    still see their own schedule and leave the other slot's runs intact."""
+    """Two layers of one split plan run at once on two streams, each with its own q, k and
+    v: the runs share the slot's workspace of partial results, so they must not mix their
+    partials (a run on another stream waits for the latest one). Then plans move to
+    another stream: every run still sees its own schedule and leaves the other slot's runs
+    intact."""
     import torch
     import ragged_attention_serving_amd as xa
-    from tests.gpu_util import from_device
-    wa = synth.paged_case([1, 30], [700, 300], 4, 2, 64, 16, mask_mode=1, seed=20)
+    from tests.gpu_util import forced_chunk, from_device
+    qo, kv = [1] * 96 + [30, 7], [2000] * 96 + [700, 300]
+    base = synth.paged_case(qo, kv, 4, 2, 64, 16, mask_mode=1, seed=20)
+    layers = []
+    for i in range(3):
+        w = synth.paged_case(qo, kv, 4, 2, 64, 16, mask_mode=1, seed=200 + i)
+        w.kv_page_indices = base.kv_page_indices
+        layers.append(w)
+    tl = [[to_device(x, "bf16", gpu) for x in (w.q, w.k_pages, w.v_pages)] for w in layers]
     wb = synth.paged_case([5, 1, 2], [20, 900, 64], 4, 2, 64, 16, mask_mode=1, seed=21)
-    ta = [to_device(x, "bf16", gpu) for x in (wa.q, wa.k_pages, wa.v_pages)]
     tb = [to_device(x, "bf16", gpu) for x in (wb.q, wb.k_pages, wb.v_pages)]
     main = torch.cuda.current_stream()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     s1.wait_stream(main)
     s2.wait_stream(main)
     plan = xa.Plan()
-    plan.plan(wa.qo_indptr, wa.kv_indptr, wa.kv_page_indices, wa.kv_last_page_len, 4, 2, 64, 16, wa.num_pages, 1,
-              stream=main)
+    with forced_chunk(64):
+        plan.plan(base.qo_indptr, base.kv_indptr, base.kv_page_indices, base.kv_last_page_len, 4, 2, 64, 16,
+                  base.num_pages, 1, stream=main)
+    info = plan.info()
+    log(f"  split schedule {info}")
+    assert info["num_merge_rows"] > 0
     outs = []
-    for st in (s1, s2):
+    for i, st in enumerate((s1, s2, main)):
         with torch.cuda.stream(st):
-            o, l = plan.run(*ta, stream=st)
-        outs.append((o, l))
+            outs.append(plan.run(*tl[i], stream=st))
     # the next plans move to stream s1; the first reuses nothing, the second reuses slot A
     with torch.cuda.stream(s1):
         plan.plan(wb.qo_indptr, wb.kv_indptr, wb.kv_page_indices, wb.kv_last_page_len, 4, 2, 64, 16,
                   wb.num_pages, 1, stream=s1)
         ob, lb = plan.run(*tb, stream=s1)
-        plan.plan(wa.qo_indptr, wa.kv_indptr, wa.kv_page_indices, wa.kv_last_page_len, 4, 2, 64, 16,
-                  wa.num_pages, 1, stream=s1)
-        oc, lc = plan.run(*ta, stream=s1)
+        plan.plan(base.qo_indptr, base.kv_indptr, base.kv_page_indices, base.kv_last_page_len, 4, 2, 64, 16,
+                  base.num_pages, 1, stream=s1)
+        oc, lc = plan.run(*tl[0], stream=s1)
     torch.cuda.synchronize()
-    ra, rla = ref.run_workload(wa)
+    refs = [ref.run_workload(w) for w in layers]
     rb, rlb = ref.run_workload(wb)
     for i, (o, l) in enumerate(outs):
-        compare(from_device(o), l.cpu().numpy().astype(np.float64), ra, rla, "bf16", label=f"A on stream {i + 1}")
+        compare(from_device(o), l.cpu().numpy().astype(np.float64), *refs[i], "bf16",
+                label=f"layer {i} on stream {('s1', 's2', 'main')[i]}")
     compare(from_device(ob), lb.cpu().numpy().astype(np.float64), rb, rlb, "bf16", label="B on s1")
-    compare(from_device(oc), lc.cpu().numpy().astype(np.float64), ra, rla, "bf16", label="A again on s1")
+    compare(from_device(oc), lc.cpu().numpy().astype(np.float64), *refs[0], "bf16", label="layer 0 again on s1")
     plan.close()

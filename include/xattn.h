@@ -196,6 +196,28 @@ XATTN_API int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, c
               void* out, float* lse, void* stream);
 
 /*
+ * xattn_run_noalloc: xattn_run for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, layouts and kernels as xattn_run; the split workspace of partial results
+ * is instead the library's static device scratch, 32 MiB per GPU (a file-scope device
+ * array that each GPU the library runs on holds until the process ends). The call makes
+ * no device or host allocation of any kind (no hipMalloc, no event, no timing records).
+ *
+ * Rules:
+ *  - runs on the stream of the handle's latest xattn_plan only (XATTN_ERR_INVALID_ARG
+ *    otherwise); the handle's plans still allocate as usual;
+ *  - a schedule whose split workspace (workspace_rows x (head_dim + 1) x 4 bytes, the
+ *    slot's capacity in a graph-stable handle) exceeds 32 MiB is rejected with
+ *    XATTN_ERR_UNSUPPORTED and a message; xattn_run has no such limit;
+ *  - every call on one GPU, from any handle, shares that GPU's scratch: calls whose
+ *    executions overlap on one GPU (runs on different streams not ordered by events)
+ *    race and give wrong results. Calls ordered on one stream are safe. The scratch is
+ *    never cleared: each run's kernels write every partial row before its merge reads it.
+ */
+XATTN_API int xattn_run_noalloc(xattn_plan_t plan, const void* q, const void* k_pages,
+                                const void* v_pages, void* out, float* lse, void* stream);
+
+/*
  * xattn_write_kv: the step before the path. Writes each request's context keys and
  * values into its pages once, so that later runs read them (page
  * "mstar.engine.resources.attn.cross": the context is written once by the encode step

@@ -32,7 +32,7 @@ XATTN_ERR_OOM = -4
 XATTN_ERR_BUSY = -5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
-EXPORTED = ("xattn_plan_create", "xattn_plan", "xattn_run", "xattn_write_kv", "xattn_plan_ready", "xattn_plan_destroy",
+EXPORTED = ("xattn_plan_create", "xattn_plan", "xattn_run", "xattn_run_noalloc", "xattn_write_kv", "xattn_plan_ready", "xattn_plan_destroy",
             "xattn_last_error", "xattn_schedule", "xattn_plan_info", "xattn_plan_set_timing",
             "xattn_plan_timing")
 STAGES = ("fp32", "decode", "mfma", "merge")
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.xattn_plan_create.restype = ctypes.c_int
     L.xattn_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.xattn_run.restype = ctypes.c_int
+    L.xattn_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.xattn_run_noalloc.restype = ctypes.c_int
     L.xattn_write_kv.argtypes = [vp, vp, vp, vp, vp, vp]
     L.xattn_write_kv.restype = ctypes.c_int
     L.xattn_plan_ready.argtypes = [vp]
@@ -195,6 +197,14 @@ def xattn_run(handle, q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, lse_ptr:
     _check(lib().xattn_run(handle, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr or None, _stream_handle(stream)))
 
 
+def xattn_run_noalloc(handle, q_ptr: int, k_ptr: int, v_ptr: int, out_ptr: int, lse_ptr: int | None,
+                      stream=None) -> None:
+    """Raw allocation-free run on device pointers (ints): the split workspace is the
+    library's static device scratch."""
+    _check(lib().xattn_run_noalloc(handle, q_ptr, k_ptr, v_ptr, out_ptr, lse_ptr or None,
+                                   _stream_handle(stream)))
+
+
 PLAN_GRAPH_STABLE = 1
 
 
@@ -290,6 +300,34 @@ class Plan:
         xattn_run(self._h, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
                   lse.data_ptr() if lse is not None else None, stream)
         return out, lse
+
+    def run_noalloc(self, q, k_pages, v_pages, out, lse=None, stream=None):
+        """Attention for one layer through xattn_run_noalloc: the caller passes out (and lse,
+        or None for no lse); nothing is allocated, the split workspace is the library's
+        static device scratch. Runs on the stream of the latest plan only."""
+        if self.meta is None:
+            raise XattnError(XATTN_ERR_INVALID_ARG, "run before plan")
+        self._check_run_tensors(q, k_pages, v_pages, out, lse)
+        xattn_run_noalloc(self._h, q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                          lse.data_ptr() if lse is not None else None, stream)
+        return out, lse
+
+    def _check_run_tensors(self, q, k_pages, v_pages, out, lse):
+        import torch
+        m = self.meta
+        tdt = torch.float32 if m["dtype"] == F32 else torch.bfloat16
+        for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("out", out)):
+            if t.dtype != tdt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous CUDA {tdt} tensor")
+        if tuple(q.shape) != (m["total_q"], m["hq"], m["d"]) or out.shape != q.shape:
+            raise ValueError(f"q and out must have shape {(m['total_q'], m['hq'], m['d'])}")
+        pool = (m["num_pages"], m["page_size"], m["hkv"], m["d"])
+        for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+            if t.numel() != int(np.prod(pool)) or t.shape[-1] != m["d"]:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {pool}")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous()
+                                or tuple(lse.shape) != (m["total_q"], m["hq"])):
+            raise ValueError(f"lse must be a contiguous CUDA float32 tensor of shape {(m['total_q'], m['hq'])}")
 
     def write_kv(self, k_src, v_src, k_pages, v_pages, stream=None):
         """Writes the planned requests' packed context rows (k_src/v_src [sum kv_len, Hkv, D])

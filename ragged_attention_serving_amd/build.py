@@ -28,7 +28,7 @@ HIP_FLAGS = [
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
              f"-I{ROCM}/include", f"-I{CSRC}", f"-I{INCLUDE}"]
 
-HIP_SOURCES = ["attn_f32.hip", "attn_decode.hip", "attn_mma.hip", "merge.hip", "write_kv.hip"]
+HIP_SOURCES = ["attn_f32.hip", "attn_decode.hip", "attn_mma.hip", "merge.hip", "write_kv.hip", "scratch.hip"]
 CXX_SOURCES = ["partition.cpp", "api.cpp"]
 
 

@@ -585,6 +585,34 @@ int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void*
   return XATTN_OK;
 }
 
+int xattn_run_noalloc(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
+                      void* out, float* lse, void* stream) {
+  int rc = check_run_args(plan, q, k_pages, v_pages, out, lse);
+  if (rc != XATTN_OK) return rc;
+  Slot& sl = plan->slot[plan->cur];
+  const Schedule& s = sl.sched;
+  if (stream != sl.plan_stream)
+    return set_err(XATTN_ERR_INVALID_ARG,
+                   "xattn_run_noalloc runs on the stream of the latest xattn_plan only");
+  const bool stable = (plan->flags & XATTN_PLAN_GRAPH_STABLE) != 0;
+  float* ws_o = nullptr;
+  float* ws_lse = nullptr;
+  if (stable ? sl.run_merge : !s.merges.empty()) {
+    // every split row is written by its chunk's unit before the merge of the same run
+    // reads it, so the scratch needs no clearing
+    const int64_t rows = stable ? sl.cap_ws_rows : s.ws_rows;
+    const size_t need = static_cast<size_t>(rows) * (sl.d + 1) * sizeof(float);
+    if (need > xattn::static_scratch_bytes())
+      return set_err(XATTN_ERR_UNSUPPORTED,
+                     "split workspace of " + std::to_string(need) + " bytes exceeds the static scratch of " +
+                         std::to_string(xattn::static_scratch_bytes()) + " bytes; use xattn_run");
+    hipError_t e = xattn::static_scratch(&ws_o);
+    if (e != hipSuccess) return hip_err(e, "hipGetSymbolAddress");
+    ws_lse = ws_o + static_cast<size_t>(rows) * sl.d;
+  }
+  return launch_run(plan, q, k_pages, v_pages, out, lse, stream, ws_o, ws_lse, false);
+}
+
 int xattn_write_kv(xattn_plan_t plan, const void* k_src, const void* v_src, void* k_pages,
                    void* v_pages, void* stream) {
   if (!plan || plan->cur < 0 || !plan->slot[plan->cur].ready)

@@ -50,4 +50,9 @@ struct WriteParams {
 int write_kv_groups(int max_kv_len);
 hipError_t launch_write_kv(const WriteParams& w, const Launch& l);
 
+// The static device scratch of xattn_run_noalloc: its size in bytes, and the current
+// device's address of it (resolved once per device, then cached).
+size_t static_scratch_bytes();
+hipError_t static_scratch(float** ptr);
+
 }  // namespace xattn

@@ -421,6 +421,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="measure the headline workload only")
     ap.add_argument("--all", action="store_true",
                     help="also measure the per-rank tensor-parallel shapes and the context write")
+    ap.add_argument("--preroll", type=float, default=0.3,
+                    help="seconds of cache flushes alone after the headline's warm-up runs, before its "
+                         "timed runs (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=24.0,
                     help="CPU seconds (summed over the worker processes) for the oracle baseline")
@@ -462,9 +465,9 @@ def main():
         print(json.dumps(measure_write(w, args.steps, args.warmup, dev)), flush=True)
         return
     log(f"[bench] measuring {args.workload}: steps={args.steps} warmup={args.warmup}")
-    # the headline is measured first in the process: after its `warmup` runs, 0.3 s of
-    # cache flushes alone bring the GPU out of its idle clocks before the timed runs
-    m = measure(w, args.steps, args.warmup, dev, preroll_s=0.3)
+    # the headline is measured first in the process: after its `warmup` runs, --preroll
+    # seconds of cache flushes alone bring the GPU out of its idle clocks before the timed runs
+    m = measure(w, args.steps, args.warmup, dev, preroll_s=args.preroll)
     res = summarize(w, m, args.steps)
     log(f"[bench] {json.dumps({k: v for k, v in res.items() if k != 'schedule'})}")
     del w, m

@@ -20,7 +20,7 @@
 //   * S^T = K Q^T (keys x the wave's 32 query columns) with Q held in registers as the
 //     B operand; a lane owns one query column and 16 of the tile's 64 keys in its
 //     accumulators (the other 16 sit in lane ^ 32), so row max and sum need one
-//     cross-lane exchange;
+//     cross-lane exchange (a VALU swap of the two 32-lane halves);
 //   * online softmax in fp32 (exp2 with log2(e) folded into the scale; the running max
 //     only moves when a tile's max exceeds it by more than 2^8, which keeps every
 //     weight below 256 and skips nearly all rescales);
@@ -72,6 +72,14 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// The value of lane ^ 32 through the VALU lane swap of 32-lane halves (no LDS round
+// trip): the swap leaves each lane its own value in one result and its partner's in the
+// other.
+__device__ __forceinline__ float xor32_f(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __lane_id() < 32 ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
 }
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
     for (int kb = 1; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    return fmaxf(mx, shfl_xor_f(mx, 32));
+    return fmaxf(mx, xor32_f(mx));
   };
 
   // ---- prologue: tile 0 in LDS (and, with three stages, tile 1 on its way)
@@ -432,7 +440,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   if constexpr (S == 3) wait_all_loads();  // no load may land in LDS after the workgroup ends
 
   // ---- finish: O / l and lse; accumulator i of block db holds dim 32db + 8(i/4) + 4half + i%4
-  const float lt = lsum + shfl_xor_f(lsum, 32);
+  const float lt = lsum + xor32_f(lsum);
   if (!valid) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;

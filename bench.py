@@ -159,8 +159,9 @@ def measure(w, steps, warmup, dev, preroll_s=0.0):
     """Plans w once, then times it two ways, each over `steps` runs:
 
     * cold (the headline): before each run 1 GiB is written to evict L2 and the Infinity
-      Cache; the run's own duration comes from HIP events around it on its stream, and
-      each kernel's from events the runtime stamps with that kernel's start and end;
+      Cache; the run's own duration comes from HIP events around it on its stream, and, in
+      a second set of `steps` such runs, each kernel's from events the runtime stamps with
+      that kernel's start and end;
     * warm: `steps` runs back to back (labelled warm), events between consecutive runs;
       every TIMING_EVERY-th run carries the kernel events.
 
@@ -191,8 +192,9 @@ def measure(w, steps, warmup, dev, preroll_s=0.0):
             flushes += 1
             torch.cuda.synchronize()
 
-    # cold runs, one at a time
-    plan.set_timing(1)
+    # cold runs, one at a time: first the runs' own durations (no per-kernel events, which
+    # add a few microseconds to each run), then the same number of runs for the kernels'
+    # own durations
     cold, cold_k = [], {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for _ in range(steps):
@@ -202,6 +204,11 @@ def measure(w, steps, warmup, dev, preroll_s=0.0):
         e1.record()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
+    plan.set_timing(1)
+    for _ in range(steps):
+        scratch.fill_(1.0)
+        run()
+        torch.cuda.synchronize()
         for st, (ms, n) in plan.timing().items():
             if n:
                 cold_k.setdefault(st, []).append(ms / n)
@@ -297,7 +304,8 @@ def summarize(w, m, steps):
             "frac": round(achieved / peak, 4), "traffic": traffic_for(dominant, w.name),
             "kernel": KERNEL_NAMES[dominant], "kernel_ms": round(kms, 5),
             "kernel_timing": f"cold: mean of the kernel's own duration over {len(m['cold'])} runs, "
-                             "each after a 1 GiB write",
+                             "each after a 1 GiB write (a second set of cold runs, after those that time "
+                             "the steps)",
             "kernel_ms_warm": round(wk, 5) if wk else None,
             "frac_warm": round(rate(wk) / peak, 4) if wk else None,
             "kernel_source_sha": source_sha(dominant),

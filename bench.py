@@ -19,8 +19,9 @@ mean duration in the cold runs (HIP events the runtime stamps with the kernel's 
 and end, on the run's stream).
 
 Prints ONE JSON line. A "sweep" object carries the four other workloads, each with its
-own value, timing and roofline (--no-sweep: headline only; --all adds per-rank tensor-
-parallel shapes and the context write).
+own value, timing and roofline (--no-sweep: headline only; --all adds cacheless span-to-span
+cross-attention, causal paged prefill, per-rank tensor-parallel shapes, graph replay of a
+32-layer decode step and the context write).
 """
 from __future__ import annotations
 
@@ -96,6 +97,21 @@ CONFIGS = {
                           "num_kv_heads": 8, "head_dim": 128, "page_size": 16, "mask": "causal",
                           "kv_bytes": 9510899712, "parallelism": "none (1 GPU)"},
 }
+CONFIGS.update({
+    "ragged_cross_spans": {"workload": "ragged_cross_spans", "requests": 32,
+                           "query_spans": "uniform 1-448 (sum 7569)", "key_spans": "uniform 256-4096 (sum 68724)",
+                           "num_qo_heads": 16, "num_kv_heads": 16, "head_dim": 128,
+                           "page_table": "identity (cacheless)", "mask": "none"},
+    "causal_prefill_paged": {"workload": "causal_prefill_paged", "requests": 16,
+                             "query_lens": "= context lens, uniform 256-4096 (sum 35086)", "num_qo_heads": 32,
+                             "num_kv_heads": 8, "head_dim": 128, "page_size": 16, "mask": "causal"},
+    "gqa_decode_causal_tp8": {"workload": "gqa_decode_causal_tp8", "requests": 256, "num_qo_heads": 4,
+                              "num_kv_heads": 1, "head_dim": 128, "page_size": 16, "mask": "causal",
+                              "note": "one rank's heads of gqa_decode_causal at tensor parallelism 8"},
+    "whisper_decode_cross_tp4": {"workload": "whisper_decode_cross_tp4", "requests": 64, "num_qo_heads": 5,
+                                 "num_kv_heads": 5, "head_dim": 64, "page_size": 16, "mask": "none",
+                                 "note": "one rank's heads of whisper_decode_cross at tensor parallelism 4"},
+})
 DTYPE_NAME = {"bf16": "bf16", "f32": "f32"}
 
 
@@ -265,6 +281,75 @@ def measure_write(w, steps, warmup, dev):
             "hbm_frac": moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def measure_graph(w, layers, steps, dev):
+    """One planned step of `layers` runs (each layer its own q, K/V cache, out and lse, the same
+    schedule), issued eagerly from the host and replayed from one captured HIP graph, back to
+    back; and the host time of planning the next step into the other slot while a replay runs
+    (the double buffer of page "mstar.engine.resources.attn.cross", force_double_buffer)."""
+    import torch
+    import ragged_attention_serving_amd as xa
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q = [to_dev(w.q, w.dtype, dev) for _ in range(layers)]
+        k = [to_dev(w.k_pages, w.dtype, dev) for _ in range(layers)]
+        v = [to_dev(w.v_pages, w.dtype, dev) for _ in range(layers)]
+        out = [torch.empty_like(x) for x in q]
+        lse = [torch.empty(x.shape[:2], dtype=torch.float32, device=dev) for x in q]
+        plan = xa.Plan()
+        plan.plan(w.qo_indptr, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, w.num_qo_heads,
+                  w.num_kv_heads, w.head_dim, w.page_size, w.num_pages, w.mask_mode, w.block_size,
+                  w.sm_scale, w.dtype, stream=s)
+
+    def step():
+        for i in range(layers):
+            plan.run(q[i], k[i], v[i], out[i], lse[i], stream=s)
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        with torch.cuda.stream(s):
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < WARMUP_SECONDS:
+                fn()
+                s.synchronize()
+            for i in range(steps):
+                ev[i].record(s)
+                fn()
+            ev[steps].record(s)
+        s.synchronize()
+        return float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+
+    eager = timed(step)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    s.synchronize()
+    graph = timed(g.replay)
+    # the next step's plan goes into the other slot while a replay reads this one
+    with torch.cuda.stream(s):
+        g.replay()
+        t0 = time.perf_counter()
+        plan.plan(w.qo_indptr, w.kv_indptr, w.kv_page_indices, w.kv_last_page_len, w.num_qo_heads,
+                  w.num_kv_heads, w.head_dim, w.page_size, w.num_pages, w.mask_mode, w.block_size,
+                  w.sm_scale, w.dtype, stream=s)
+        plan_ms = (time.perf_counter() - t0) * 1e3
+    s.synchronize()
+    # the captured graph still replays the first slot's schedule: its outputs equal an eager run
+    ref_out = [x.clone() for x in out]
+    g.replay()
+    s.synchronize()
+    same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(out, ref_out))
+    del g
+    plan.close()
+    kv_bytes = int(w.kv_lens().sum()) * w.num_kv_heads * w.head_dim * 2 * (2 if w.dtype == "bf16" else 4)
+    return {"workload": f"graph_replay:{w.name}", "layers": layers, "eager_ms_per_step": round(eager, 5),
+            "graph_ms_per_step": round(graph, 5), "graph_speedup": round(eager / graph, 3),
+            "GBps_eager": round(layers * kv_bytes / (eager * 1e-3) / 1e9, 1),
+            "GBps_graph": round(layers * kv_bytes / (graph * 1e-3) / 1e9, 1),
+            "plan_ms_during_replay": round(plan_ms, 3), "replay_after_next_plan_unchanged": same,
+            "note": "warm, back to back; each layer reads its own K/V cache"}
+
+
 def summarize(w, m, steps):
     """One workload's entry: value from the cold runs (median), warm beside it, and the
     roofline of the dominant kernel from its cold durations."""
@@ -428,7 +513,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-sweep", action="store_true", help="measure the headline workload only")
     ap.add_argument("--all", action="store_true",
-                    help="also measure the per-rank tensor-parallel shapes and the context write")
+                    help="also measure cacheless span-to-span cross-attention, causal paged prefill, the "
+                         "per-rank tensor-parallel shapes, graph replay of a 32-layer decode step and the "
+                         "context write")
     ap.add_argument("--preroll", type=float, default=0.3,
                     help="seconds of cache flushes alone after the headline's warm-up runs, before its "
                          "timed runs (0: none)")
@@ -450,7 +537,7 @@ def main():
     import torch
     from ragged_attention_serving_amd import synth
 
-    all_workloads = {**synth.WORKLOADS, **synth.TP_WORKLOADS}
+    all_workloads = {**synth.WORKLOADS, **synth.NEXT_WORKLOADS, **synth.TP_WORKLOADS}
     if args.copy_calibration:
         dev = torch.device("cuda:0")
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -500,7 +587,7 @@ def main():
     if not args.no_sweep:
         names = [n for n in synth.WORKLOADS if n != args.workload]
         if args.all:
-            names += [n for n in synth.TP_WORKLOADS if n != args.workload]
+            names += [n for n in {**synth.NEXT_WORKLOADS, **synth.TP_WORKLOADS} if n != args.workload]
         sweep = {}
         for name in names:
             log(f"[bench] sweep: generating {name}")
@@ -515,6 +602,11 @@ def main():
             del ws, ms
             torch.cuda.empty_cache()
         if args.all:
+            log("[bench] sweep: graph replay")
+            gr = measure_graph(synth.TP_WORKLOADS["whisper_decode_cross_tp4"](0), 32, args.steps, dev)
+            sweep[gr["workload"]] = gr
+            log(f"[bench] {json.dumps(gr)}")
+            torch.cuda.empty_cache()
             log("[bench] sweep: context write")
             wr = measure_write(synth.WORKLOADS["whisper_decode_cross"](0), args.steps, None, dev)
             sweep[wr["workload"]] = wr

@@ -327,12 +327,41 @@ def whisper_decode_tp4(seed: int = 0) -> Workload:
                       name="whisper_decode_cross_tp4", sm_scale=1.0 / 8.0)
 
 
+def ragged_cross_spans(seed: int = 0) -> Workload:
+    """Cacheless span-to-span cross-attention (page "mstar.engine.resources.attn.ragged.base",
+    RaggedCrossAttnManager: each request attends from its query span to its own key span, no
+    page table): 32 requests, query spans U[1,448], key spans U[256,4096], 16 heads,
+    head_dim 128, bf16, no mask."""
+    rng = np.random.default_rng(seed)
+    qo = rng.integers(1, 448, 32, endpoint=True)
+    kv = rng.integers(256, 4096, 32, endpoint=True)
+    return ragged_cross_case(qo, kv, 16, 128, dtype="bf16", seed=seed, name="ragged_cross_spans")
+
+
+def causal_prefill_paged(seed: int = 0) -> Workload:
+    """Multi-token causal prefill over a paged cache (page "mstar.engine.resources.attn.config",
+    AttentionStep.causal; page "mstar.model.components.attention", grouped KV heads): 16 requests
+    whose whole context is new (qo_len = kv_len, uniform 256-4096), 32 query / 8 KV heads,
+    head_dim 128, bf16, page_size 16, shuffled pages."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(256, 4096, 16, endpoint=True)
+    return paged_case(lens, lens, 32, 8, 128, 16, dtype="bf16", mask_mode=MASK_CAUSAL, seed=seed,
+                      rng=rng, name="causal_prefill_paged")
+
+
 WORKLOADS = {
     "tiny_cross_f32": tiny_cross,
     "whisper_decode_cross": whisper_decode,
     "ragged_prefill_cross": ragged_prefill,
     "block_causal_ragged": block_causal,
     "gqa_decode_causal": gqa_decode,
+}
+
+# the variants of the path beyond the five workloads: cacheless span-to-span cross-attention
+# and multi-token causal prefill over a paged cache, measured by `bench.py --all`
+NEXT_WORKLOADS = {
+    "ragged_cross_spans": ragged_cross_spans,
+    "causal_prefill_paged": causal_prefill_paged,
 }
 
 # per-rank shapes of tensor parallelism over heads, measured on one GPU

@@ -66,6 +66,18 @@ def test_tensor_parallel_rank_shapes(gpu):
     _full_by_request(synth.gqa_decode_tp8(0), gpu)
 
 
+def test_ragged_cross_spans_full(gpu):
+    """Cacheless span-to-span cross-attention at full size: 32 requests, query spans of
+    1-448 tokens over key spans of 256-4096, 16 heads, head_dim 128."""
+    _full_by_request(synth.ragged_cross_spans(0), gpu)
+
+
+def test_causal_prefill_paged_full(gpu):
+    """Multi-token causal prefill over a paged cache at full size: 16 requests of 256-4096
+    new tokens, 32 query / 8 KV heads, head_dim 128, page_size 16."""
+    _full_by_request(synth.causal_prefill_paged(0), gpu)
+
+
 def test_gqa_decode_full(gpu):
     """The GQA decode at full size (9.5 GB of K and V, split contexts merged): every
     request, every head."""

@@ -35,6 +35,11 @@ def test_generator_self_check():
     assert kv.min() >= 512 and kv.max() <= 32768
     qo = synth.ragged_prefill_query_lengths(np.random.default_rng(0))
     assert int(qo.sum()) == 7569 and list(qo[:4]) == [382, 286, 229, 121]
+    w6 = synth.ragged_cross_spans(0)
+    assert int(w6.qo_indptr[-1]) == 7569 and int(w6.kv_indptr[-1]) == 68724
+    assert list(w6.qo_lens()[:4]) == [382, 286, 229, 121] and w6.k_pages.shape == (68724, 1, 16, 128)
+    w7_lens = np.random.default_rng(0).integers(256, 4096, 16, endpoint=True)
+    assert int(w7_lens.sum()) == 35086
     w2 = synth.whisper_decode(0)
     assert list(set(w2.kv_lens())) == [1500] and int(w2.kv_indptr[-1]) == 6016
     assert set(w2.kv_last_page_len) == {12} and w2.num_pages == 6016

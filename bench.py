@@ -470,14 +470,14 @@ def _request_work(w):
 
 def cpu_baseline(w, cpu_seconds=24.0):
     """The fp64 oracle as it stands, on this host's cores: one process per core (at most 16),
-    each taking whole requests (all heads) in turn for cpu_seconds / processes (at least 2 s)
-    of wall time.
+    each taking whole requests (all heads) in turn for cpu_seconds / processes (at least 1 s)
+    of wall time (a process finishes the request it is on).
     Must run before the process touches the GPU (the workers are forked)."""
     import multiprocessing as mp
     global _CPU_W
     _CPU_W = w
     n = max(1, min(16, len(os.sched_getaffinity(0))))
-    wall = max(2.0, cpu_seconds / n)
+    wall = max(1.0, cpu_seconds / n)
     ctx = mp.get_context("fork")
     with ctx.Pool(n) as pool:
         t0 = time.perf_counter()

@@ -14,7 +14,9 @@
 // (key rows of head_dim values) with the 16-byte chunks of each row XOR-swizzled by the
 // row, so that the MFMA operand reads below hit distinct LDS banks. The page indices of
 // the unit's pages are staged in LDS once, so the tile loop issues no vector-memory
-// operation other than the tile loads themselves.
+// operation other than the tile loads themselves. The kernel is instantiated per table
+// kind (a page table, or the identity table of packed spans), so its tile loop carries
+// only that table's address arithmetic.
 //
 // Math, per tile and wave:
 //   * S^T = K Q^T (keys x the wave's 32 query columns) with Q held in registers as the
@@ -74,12 +76,17 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The value of lane ^ 32 through the VALU lane swap of 32-lane halves (no LDS round
-// trip): the swap leaves each lane its own value in one result and its partner's in the
-// other.
-__device__ __forceinline__ float xor32_f(float x) {
+// Lane l and lane l ^ 32 combined through the VALU swap of the 32-lane halves (no LDS
+// round trip): the swap leaves each lane its own value in one result and its partner's in
+// the other, so a symmetric operation on the two results needs no lane select (and both
+// lanes of a pair get the same bits).
+__device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __lane_id() < 32 ? __uint_as_float(r[1]) : __uint_as_float(r[0]);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
@@ -92,7 +99,7 @@ __device__ __forceinline__ void wait_loads_but_one_tile() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NIW));
 }
 
-template <int D, int MASK, int NW, int BN, bool BUF>
+template <int D, int MASK, int NW, int BN, bool BUF, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p) {
   using C = Cfg<D, NW, BN>;
   constexpr int NKB = C::NKB, NST = C::NST;
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   const int lim = valid ? min(last_visible(MASK, p.block, qo_len, kv_len, qi), kv1 - 1) : kv1 - 1;
 
   const int ntiles = kv1 > kv0 ? (kv1 - kv0 + BN - 1) / BN : 0;
-  const bool paged = p.pages != nullptr;
+  constexpr bool paged = PAGED;  // a page table, or the identity table (no gather)
 
   // ---- the unit's page indices, staged in LDS once (at most kMmaMaxPages of them)
   __shared__ int spg[kMmaMaxPages];
@@ -277,19 +284,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  // running max (log2 units) and this lane's partial row sum, both in fp32
+  // running max (log2 units) and this lane's partial row sum, both in fp32; the max only
+  // changes in the rare rescale, which also updates what each tile reads of it: the
+  // exponent offset (minus the max, or 0 while no key has been seen) and the raw-score
+  // level above which a tile moves the max
   float m = -INFINITY, lsum = 0.f;
+  float neg_m = 0.f, raw_level = -INFINITY;
+  const float inv_scale = 1.f / p.scale_log2;
 
-  // max over a lane's query column: its 32 accumulators, then the 32 in lane ^ 32
+  // max of the raw scores over a lane's query column: its 32 accumulators, then the 32 in
+  // lane ^ 32 (IEEE maximum: -inf for masked keys, no quieting step on its inputs)
   auto column_max = [&](const f32x16_t (&s)[NKB]) __attribute__((always_inline)) -> float {
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float mx = __builtin_elementwise_maximum(s[0][0], s[0][1]);
 #pragma unroll
-    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+    for (int i = 2; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[0][i]);
 #pragma unroll
     for (int kb = 1; kb < NKB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    return fmaxf(mx, xor32_f(mx));
+      for (int i = 0; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, s[kb][i]);
+    return pair_max(mx);
   };
 
   // ---- prologue: tile 0 in LDS (and, with three stages, tile 1 on its way)
@@ -392,9 +405,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
           for (int i = 0; i < 16; ++i)
             if (32 * kb + 8 * (i / 4) + (i % 4) > d) sc[kb][i] = -INFINITY;
       }
-      const float mxs = column_max(sc) * p.scale_log2;
-      if (__any(mxs > m + kRescaleSlack)) {
-        const float mn = fmaxf(m, mxs);
+      const float mx = column_max(sc);
+      if (__any(mx > raw_level)) {
+        const float mn = fmaxf(m, mx * p.scale_log2);
         const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
         lsum *= alpha;
 #pragma unroll
@@ -402,8 +415,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
         m = mn;
+        neg_m = mn == -INFINITY ? 0.f : -mn;
+        raw_level = (mn + kRescaleSlack) * inv_scale;
       }
-      const float mu = m == -INFINITY ? 0.f : m;
 
       // probabilities, row sums, and the bf16 B operands for P V (k-step = 16 keys)
       bf16x8_t pb[NST];
@@ -412,7 +426,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(sc[b / 2][8 * (b % 2) + e], p.scale_log2, -mu));
+          pv[e] = fast_exp2(fmaf(sc[b / 2][8 * (b % 2) + e], p.scale_log2, neg_m));
           lsum += pv[e];
         }
         const uint4 packed = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -440,7 +454,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   if constexpr (S == 3) wait_all_loads();  // no load may land in LDS after the workgroup ends
 
   // ---- finish: O / l and lse; accumulator i of block db holds dim 32db + 8(i/4) + 4half + i%4
-  const float lt = lsum + xor32_f(lsum);
+  const float lt = pair_sum(lsum);
   if (!valid) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
@@ -471,15 +485,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mma_kernel(AttnParams p)
   }
 }
 
-template <int D, int NW, int BN, bool BUF>
-hipError_t launch_dwb(const AttnParams& p, const Launch& l) {
+template <int D, int NW, int BN, bool BUF, bool PAGED>
+hipError_t launch_dwbp(const AttnParams& p, const Launch& l) {
   const dim3 grid(p.num_units), block(64 * NW);
   switch (p.mask) {
-    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW, BN, BUF>, grid, block, p, l);
-    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW, BN, BUF>, grid, block, p, l);
-    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW, BN, BUF>, grid, block, p, l);
+    case 0: return launch_kernel(attn_mma_kernel<D, 0, NW, BN, BUF, PAGED>, grid, block, p, l);
+    case 1: return launch_kernel(attn_mma_kernel<D, 1, NW, BN, BUF, PAGED>, grid, block, p, l);
+    case 2: return launch_kernel(attn_mma_kernel<D, 2, NW, BN, BUF, PAGED>, grid, block, p, l);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D, int NW, int BN, bool BUF>
+hipError_t launch_dwb(const AttnParams& p, const Launch& l) {
+  if (p.pages != nullptr) return launch_dwbp<D, NW, BN, BUF, true>(p, l);
+  return launch_dwbp<D, NW, BN, BUF, false>(p, l);
 }
 
 // buffer loads (32-bit offsets) when both pools span less than 4 GB

@@ -66,9 +66,10 @@ def run_gpu(w, device, chunk=0, tensors=None, plan=None, want_lse=True):
     return from_device(out), (lse.cpu().numpy().astype(np.float64) if lse is not None else None), plan
 
 
-def compare(out, lse, ref_out, ref_lse, dtype, rows=None, label=""):
-    """Asserts parity within the dtype's tolerance on the given rows (all if None)."""
-    tol_o, tol_l = TOL[dtype]
+def compare(out, lse, ref_out, ref_lse, dtype, rows=None, label="", tol=None):
+    """Asserts parity within the dtype's tolerance (or ``tol`` = (out, lse) where a test
+    derives its own) on the given rows (all if None)."""
+    tol_o, tol_l = TOL[dtype] if tol is None else tol
     if rows is not None:
         out, lse, ref_out, ref_lse = out[rows], lse[rows], ref_out[rows], ref_lse[rows]
     assert not np.isnan(out).any(), f"{label}: NaN in out"

@@ -187,10 +187,12 @@ XATTN_API int xattn_plan_create(xattn_plan_t* plan, int32_t flags);
  * Graph capture (page "mstar.engine.resources.attn.cross", force_double_buffer: the plan
  * keeps two buffers so that a captured graph can read one while the next plan fills the
  * other). A run on the plan's own stream with timing off issues kernel launches only, so
- * it may be captured into a HIP graph. A replay repeats the captured schedule with the
- * captured pointers: it stays valid through the handle's next xattn_plan (which fills
- * the other slot) and must not be replayed after the one after that, which reuses (and
- * may reallocate) the slot it reads.
+ * it may be captured into a HIP graph, provided that the slot's latest run of a split
+ * schedule was on that stream too (otherwise the run first waits for an event recorded
+ * on the other stream, which a capture cannot take in). A replay repeats the captured
+ * schedule with the captured pointers: it stays valid through the handle's next
+ * xattn_plan (which fills the other slot) and must not be replayed after the one after
+ * that, which reuses (and may reallocate) the slot it reads.
  */
 XATTN_API int xattn_run(xattn_plan_t plan, const void* q, const void* k_pages, const void* v_pages,
               void* out, float* lse, void* stream);

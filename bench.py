@@ -171,7 +171,7 @@ def _stats(xs):
             "mean_ms": round(float(np.mean(xs)), 5), "runs": len(xs)}
 
 
-def measure(w, steps, warmup, dev, preroll_s=0.0):
+def measure(w, steps, warmup, dev, preroll_s=0.0, keep_rows=None):
     """Plans w once, then times it two ways, each over `steps` runs:
 
     * cold (the headline): before each run 1 GiB is written to evict L2 and the Infinity
@@ -183,7 +183,8 @@ def measure(w, steps, warmup, dev, preroll_s=0.0):
 
     `warmup` untimed runs come first (None: as many as fill WARMUP_SECONDS), then, when
     preroll_s > 0, cache flushes alone for that long (the GPU leaves its idle clocks only
-    under load; a flush is not a run)."""
+    under load; a flush is not a run). keep_rows (query-row indices) returns those rows of
+    the last timed run's out and lse."""
     import torch
     import ragged_attention_serving_amd as xa
 
@@ -244,11 +245,16 @@ def measure(w, steps, warmup, dev, preroll_s=0.0):
     warm = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     warm_k = {st: ms / n for st, (ms, n) in plan.timing().items() if n}
     plan.set_timing(0)
+    kept = None
+    if keep_rows is not None:
+        idx = torch.as_tensor(np.asarray(keep_rows, np.int64), device=dev)
+        kept = (out.index_select(0, idx).float().cpu().numpy().astype(np.float64),
+                lse.index_select(0, idx).cpu().numpy().astype(np.float64))
     plan.close()
     del q, k, v, out, lse
     return dict(plan_ms=plan_ms, info=info, warmup=warmed, preroll_flushes=flushes,
                 cold=cold, cold_kernel={st: float(np.mean(x)) for st, x in cold_k.items()},
-                warm=warm, warm_kernel=warm_k, warm_wall_ms=wall_ms)
+                warm=warm, warm_kernel=warm_k, warm_wall_ms=wall_ms, kept=kept)
 
 
 def measure_write(w, steps, warmup, dev):
@@ -423,8 +429,13 @@ def traffic_for(stage: str, workload: str):
 _CPU_W = None  # the workload, shared with forked workers
 
 
+KEEP_BYTES = 64 << 20  # oracle results a CPU-baseline worker keeps for the parity check
+
+
 def _cpu_worker(args):
-    """One process: oracle passes over requests start, start+step, ... for wall_s seconds."""
+    """One process: oracle passes over requests start, start+step, ... for wall_s seconds.
+    Keeps the results of its first pass over each request (fp32, up to KEEP_BYTES) so that
+    the bench can compare them with the GPU's outputs of the timed runs."""
     start, step, wall_s = args
     try:
         from threadpoolctl import threadpool_limits
@@ -435,16 +446,22 @@ def _cpu_worker(args):
     w = _CPU_W
     work = _request_work(w)
     done_work, done_req, i = 0, 0, start
+    kept, kept_bytes = {}, 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < wall_s:
         r = i % w.batch_size
-        ref.run_workload(w, requests=[r])
+        o, l = ref.run_workload(w, requests=[r])
         done_work += int(work[r])
         done_req += 1
         i += step
+        a, b = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
+        nbytes = (b - a) * w.num_qo_heads * (w.head_dim + 1) * 4
+        if r not in kept and kept_bytes + nbytes <= KEEP_BYTES:
+            kept[r] = (o[a:b].astype(np.float32), l[a:b].astype(np.float32))
+            kept_bytes += nbytes
     el = time.perf_counter() - t0
     del ctx  # (the limit only needs to hold while this worker runs)
-    return done_work, done_req, el
+    return done_work, done_req, el, kept
 
 
 def _request_work(w):
@@ -472,7 +489,9 @@ def cpu_baseline(w, cpu_seconds=24.0):
     """The fp64 oracle as it stands, on this host's cores: one process per core (at most 16),
     each taking whole requests (all heads) in turn for cpu_seconds / processes (at least 1 s)
     of wall time (a process finishes the request it is on).
-    Must run before the process touches the GPU (the workers are forked)."""
+    Must run before the process touches the GPU (the workers are forked).
+    Returns the baseline record and the oracle's results per request it covered
+    ({r: (out rows, lse rows)}, fp32), for the parity check of the timed outputs."""
     import multiprocessing as mp
     global _CPU_W
     _CPU_W = w
@@ -485,6 +504,9 @@ def cpu_baseline(w, cpu_seconds=24.0):
         el = time.perf_counter() - t0
     done_work = sum(p[0] for p in parts)
     done_req = sum(p[1] for p in parts)
+    kept = {}
+    for p in parts:
+        kept.update(p[3])
     work = _request_work(w)
     decode = bool(np.all(w.qo_lens() * (w.num_qo_heads // w.num_kv_heads) <= 8)) and w.dtype == "bf16"
     scale, unit = (1e9, "GB/s") if decode else (1e12, "TFLOP/s")
@@ -492,7 +514,27 @@ def cpu_baseline(w, cpu_seconds=24.0):
             "host_cores": host_cores(),
             "sample": f"{done_req} request passes (all {w.num_qo_heads} heads each, {done_req / w.batch_size:.2f} "
                       f"x the workload's {w.batch_size} requests, taken in turn) by {n} processes in {el:.1f} s",
-            "workload_work": int(work.sum())}
+            "workload_work": int(work.sum())}, kept
+
+
+def timed_output_parity(w, kept, rows_out):
+    """Compares the GPU's out and lse of the timed runs (rows_out: the checked requests'
+    rows, in request order) with the oracle results the CPU baseline kept, at the parity
+    tolerance of the tests (bf16: 2e-2 on out, fp32: 1e-5; 1e-3 on lse)."""
+    tol_o, tol_l = (2e-2, 1e-3) if w.dtype == "bf16" else (1e-5, 1e-3)
+    reqs = sorted(kept)
+    go, gl = rows_out
+    ro = np.concatenate([kept[r][0] for r in reqs]).astype(np.float64)
+    rl = np.concatenate([kept[r][1] for r in reqs]).astype(np.float64)
+    fin = np.isfinite(rl)
+    err_o = float(np.max(np.abs(go - ro))) if ro.size else 0.0
+    err_l = float(np.max(np.abs(gl[fin] - rl[fin]))) if fin.any() else 0.0
+    ok = bool(err_o <= tol_o and err_l <= tol_l and np.array_equal(np.isfinite(gl), fin)
+              and not np.isnan(go).any())
+    return {"requests": len(reqs), "of": w.batch_size, "rows": int(ro.shape[0]) if ro.size else 0,
+            "max_abs_out_err": err_o, "max_abs_lse_err": err_l, "tol": [tol_o, tol_l], "pass": ok,
+            "what": "out and lse of the last timed run against the fp64 oracle results computed by "
+                    "the CPU-baseline leg for the same requests"}
 
 
 def host_cores():
@@ -549,11 +591,11 @@ def main():
         return
     log(f"[bench] generating {args.workload}")
     w = all_workloads[args.workload](0)
-    cpu_line = None
+    cpu_line, kept = None, {}
     if not (args.no_cpu_baseline or args.context_write):
         # before anything touches the GPU: the oracle's worker processes are forked
         log(f"[bench] timing the CPU oracle on {args.workload}")
-        cpu_line = cpu_baseline(w, args.cpu_seconds)
+        cpu_line, kept = cpu_baseline(w, args.cpu_seconds)
         log(f"[bench] cpu baseline {json.dumps(cpu_line)}")
     dev = torch.device("cuda:0")
     if args.context_write:
@@ -562,8 +604,12 @@ def main():
     log(f"[bench] measuring {args.workload}: steps={args.steps} warmup={args.warmup}")
     # the headline is measured first in the process: after its `warmup` runs, --preroll
     # seconds of cache flushes alone bring the GPU out of its idle clocks before the timed runs
-    m = measure(w, args.steps, args.warmup, dev, preroll_s=args.preroll)
+    keep_rows = None
+    if kept:
+        keep_rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in sorted(kept)])
+    m = measure(w, args.steps, args.warmup, dev, preroll_s=args.preroll, keep_rows=keep_rows)
     res = summarize(w, m, args.steps)
+    parity = timed_output_parity(w, kept, m["kept"]) if kept else None
     log(f"[bench] {json.dumps({k: v for k, v in res.items() if k != 'schedule'})}")
     del w, m
     torch.cuda.empty_cache()
@@ -584,6 +630,9 @@ def main():
         line["hbm_compulsory"] = res["hbm_compulsory"]
     if cpu_line is not None:
         line["cpu_baseline"] = cpu_line
+    if parity is not None:
+        line["parity"] = parity
+        log(f"[bench] parity of the timed outputs: {json.dumps(parity)}")
     if not args.no_sweep:
         names = [n for n in synth.WORKLOADS if n != args.workload]
         if args.all:

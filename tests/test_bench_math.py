@@ -37,3 +37,23 @@ def test_summary_value_and_roofline():
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["kernel"] == "attn_decode_kernel"
     assert abs(roof["achieved"] - 491.52e6 / 0.0768e-3 / 1e9) < 0.01
     assert abs(roof["frac"] - roof["achieved"] / 8000.0) < 1e-4
+
+
+def test_timed_output_parity_uses_the_baseline_results():
+    """The CPU-baseline leg keeps the oracle's results of the requests it covered; the
+    bench compares them with the rows of the timed run: the oracle's own rows pass, a
+    perturbed row fails."""
+    w = synth.tiny_cross(0)
+    line, kept = bench.cpu_baseline(w, cpu_seconds=1.0)
+    assert line["kind"] == "oracle" and sorted(kept) == list(range(w.batch_size))
+    from oracle import ref
+    ro, rl = ref.run_workload(w)
+    rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in sorted(kept)])
+    good = bench.timed_output_parity(w, kept, (ro[rows], rl[rows]))
+    assert good["pass"] and good["rows"] == len(rows) and good["max_abs_out_err"] < 1e-6
+    bad_o = ro[rows].copy()
+    bad_o[0, 0, 0] += 1e-4  # past the fp32 gate of 1e-5
+    assert not bench.timed_output_parity(w, kept, (bad_o, rl[rows]))["pass"]
+    bad_l = rl[rows].copy()
+    bad_l[-1, -1] += 2e-3
+    assert not bench.timed_output_parity(w, kept, (ro[rows], bad_l))["pass"]

@@ -97,3 +97,35 @@ def test_run_without_plan_is_rejected():
 
 def test_destroy_null_is_a_no_op():
     xa.lib().xattn_plan_destroy(None)
+
+
+def test_binding_raises_without_the_library():
+    """No fallback: without libxattn.so every entry point of the binding raises."""
+    import subprocess
+    import sys
+    code = (
+        "import ragged_attention_serving_amd as xa\n"
+        "xa.LIB_PATH = '/nonexistent/libxattn.so'\n"
+        "xa._lib = None\n"
+        "import numpy as np\n"
+        "for call in (lambda: xa.lib(), lambda: xa.Plan().plan(np.array([0, 1], np.int32), np.array([0, 1], np.int32),"
+        " None, None, 1, 1, 64, 16, 1)):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except RuntimeError as e:\n"
+        "        assert 'missing' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('no error')\n"
+        "print('raised')\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0 and "raised" in r.stdout, r.stderr[-2000:]
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       timeout=300, cwd=root)
+    assert r.returncode == 2 and "one GPU only" in r.stderr, (r.returncode, r.stderr[-2000:])

@@ -55,6 +55,8 @@ struct Cfg {
   static constexpr int LPR = 64 / RPI;         // lanes per key row in a load
   static constexpr int NIW = BN / RPI / NW;    // load instructions per wave per tile (K or V)
   static_assert(NIW * RPI * NW == BN, "tile split across waves");
+  // the per-row table path gives each lane of a wave one key of the tile
+  static_assert(BN <= 64, "at most one key per lane in a tile");
   static constexpr int TILE = BN * ROWB;       // bytes of one K (or V) tile
   // 16-byte chunk swizzle: chunk c of key row r is stored in slot c ^ swz(r). With 64
   // banks of 4 bytes (a 256-byte window; a D=128 row fills one, a D=64 row half of one):

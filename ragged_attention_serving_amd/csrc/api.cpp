@@ -112,6 +112,8 @@ struct xattn_plan_s {
 
 namespace {
 
+// Grows a buffer geometrically. Freeing the old one is safe while runs may still read
+// it: hipFree and hipHostFree synchronise the device before they release memory.
 int ensure(void** ptr, size_t* cap, size_t need, bool pinned) {
   if (*cap >= need && *ptr) return XATTN_OK;
   size_t want = need < 4096 ? 4096 : need + need / 4;

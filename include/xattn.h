@@ -123,7 +123,8 @@ enum xattn_status {
  * num_pages       pages in the K and V pools; every referenced page must lie below it.
  * mask_mode       an xattn_mask_mode. CAUSAL and BLOCK_CAUSAL need qo_len <= kv_len.
  * block_size      >= 1, read only for BLOCK_CAUSAL.
- * sm_scale        score scale; <= 0 means 1 / sqrt(head_dim).
+ * sm_scale        score scale; <= 0 means 1 / sqrt(head_dim); NaN, infinity and scales
+ *                 whose product with log2(e) overflows are rejected.
  * dtype           an xattn_dtype.
  * stream          hipStream_t for the host-to-device copy (NULL: the null stream).
  *

@@ -114,6 +114,9 @@ int build_schedule(const PlanArgs& a, Schedule& s, std::string& err) {
   if (a.tile_rows != 0 && a.tile_rows != 128 && a.tile_rows != 256)
     return fail(err, kErrInvalid, "tile_rows must be 128 or 256");
   s.tile_rows = a.tile_rows ? a.tile_rows : kMmaRows;
+  // the kernels take the scale in log2 units: it must stay finite there
+  if (std::isnan(a.sm_scale) || (a.sm_scale > 0.f && !std::isfinite(a.sm_scale * 1.4426950408889634f)))
+    return fail(err, kErrInvalid, "sm_scale must be finite (<= 0 selects 1/sqrt(head_dim))");
 
   const int g = a.hq / a.hkv;
   s.group = g;

@@ -129,3 +129,12 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
                        timeout=300, cwd=root)
     assert r.returncode == 2 and "one GPU only" in r.stderr, (r.returncode, r.stderr[-2000:])
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), 3e38])
+def test_plan_rejects_a_scale_that_is_not_finite(scale):
+    h = ctypes.c_void_p()
+    with pytest.raises(xa.XattnError) as e:
+        xa.xattn_plan(h, [0, 1], [0, 1], [0], [4], 2, 2, 64, 4, 1, sm_scale=scale, stream=0)
+    assert e.value.code == xa.XATTN_ERR_INVALID_ARG and not h.value
+    assert "sm_scale" in xa.xattn_last_error()
